@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the attention backward on one MI355X.
+
+Workload: causal, bf16, B=2, H=32, n=m=4096, d=dv=128, seed 2, scale
+1/sqrt(128).  A step is one backward pass (D preprocess, dK/dV kernel, dQ
+kernel) over inputs already resident in HBM; O and LSE come from the
+forward kernel, which runs before the timed region and is timed on its own
+as context.  FLOPs follow the convention 2nm(3d + 2dv) per head (10nmd when
+d = dv), halved for causal.
+
+Prints one JSON line.  Options: --steps K --warmup W --gpus N (N must be 1)
+--workload NAME --no-cpu-baseline --cpu-heads H.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+
+
+def bwd_flops(w) -> float:
+    f = 2.0 * w.n * w.m * (3 * w.d + 2 * w.dv) * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def fwd_flops(w) -> float:
+    f = 2.0 * w.n * w.m * (w.d + w.dv) * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def dkdv_flops(w) -> float:
+    # S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
+    f = 2.0 * w.n * w.m * (2 * w.d + 2 * w.dv) * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def dq_flops(w) -> float:
+    # S, dP recomputed, dQ += dS K
+    f = 2.0 * w.n * w.m * (2 * w.d + w.dv) * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def bwd_bytes(w) -> float:
+    """Algorithmic HBM bytes of one backward: read Q,K,V,O,dO (bf16) and
+    LSE; write dQ,dK,dV (bf16); D and rescaled LSE written and read once."""
+    e = 2
+    heads = w.B * w.H
+    qk = heads * (w.n * w.d + w.m * w.d) * e
+    vo = heads * (w.m * w.dv + 2 * w.n * w.dv) * e
+    grads = heads * (w.n * w.d + w.m * w.d + w.m * w.dv) * e
+    rows = heads * w.n * 4 * (1 + 2 * 2)
+    return float(qk + vo + grads + rows)
+
+
+def time_loop(fn, steps, torch):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, inputs, heads_wanted):
+    """The float64 oracle's backward on a bounded sample of the workload's
+    heads, on the host cores; reported in the metric's unit."""
+    import numpy as np
+    import oracle
+    threads = oracle.num_threads()
+    nh = max(1, min(heads_wanted or threads, w.B * w.H))
+    q, k, v, do = (t.reshape(w.B * w.H, *t.shape[2:])[:nh].double().numpy() for t in inputs)
+    q, k, v, do = (np.ascontiguousarray(x[None]) for x in (q, k, v, do))
+    t0 = time.perf_counter()
+    oracle.attn_bwd(q, k, v, do, scale=w.softmax_scale, causal=w.causal)
+    dt = time.perf_counter() - t0
+    per_head = bwd_flops(w) / (w.B * w.H)
+    return {
+        "value": per_head * nh / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{nh} of {w.B * w.H} heads of {w.name} (float64 backward incl. recomputing "
+                  f"P, O, D), {dt:.1f} s wall on {threads} OpenMP threads",
+        "seconds": dt, "heads": nh,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (batch, head) is independent; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attn_bwd_amd as attn
+    from transformer_attn_bwd_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: {w.describe()}", file=sys.stderr, flush=True)
+
+    inputs_cpu = make_inputs(w, "cpu")
+    q, k, v, do = (t.to(dev) for t in inputs_cpu)
+    o, lse = attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal)
+    ws = torch.empty(max(attn.bwd_workspace_bytes(w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype), 1),
+                     dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def bwd_step(stages=None):
+        attn.bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, workspace=ws,
+                 dq=dq, dk=dk, dv=dv, stages=stages)
+
+    def fwd_step():
+        attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        fwd_step()
+        bwd_step()
+    torch.cuda.synchronize()
+    print("bench: warmup done", file=sys.stderr, flush=True)
+
+    # timed region: K backward steps, bracketed by device synchronisation
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ms = time_loop(bwd_step, args.steps, torch)
+    t_wall = time.perf_counter() - t_wall
+    print(f"bench: {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    ok = bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
+
+    # per-kernel average launch durations (HIP events on the launch stream)
+    kern_ms = {
+        "preprocess": time_loop(lambda: bwd_step(["preprocess"]), args.steps, torch),
+        "dkdv": time_loop(lambda: bwd_step(["dkdv"]), args.steps, torch),
+        "dq": time_loop(lambda: bwd_step(["dq"]), args.steps, torch),
+    }
+    fwd_ms = time_loop(fwd_step, args.steps, torch)
+    # restore outputs of a whole backward after the single-stage runs
+    bwd_step()
+    torch.cuda.synchronize()
+
+    flops = bwd_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    dk_tf = dkdv_flops(w) / (kern_ms["dkdv"] * 1e-3) / 1e12
+    dominant = max(("dkdv", "dq"), key=lambda kname: kern_ms[kname])
+    dom_flops = dkdv_flops(w) if dominant == "dkdv" else dq_flops(w)
+    dom_tf = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
+
+    result = {
+        "metric": "attn backward TFLOP/s (bf16, causal, d=128, N=4096) + % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, see transformer_attn_bwd_amd/workloads.py)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "m": w.m, "d": w.d,
+                   "dv": w.dv, "causal": w.causal, "seed": w.seed, "scale": w.softmax_scale,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": flops,
+        "kernels_ms": {k_: round(v_, 4) for k_, v_ in kern_ms.items()},
+        "fwd": {"ms": round(fwd_ms, 4),
+                "tflops": round(fwd_flops(w) / (fwd_ms * 1e-3) / 1e12, 2)},
+        "roofline": {
+            "kernel": f"bwd_{dominant}",
+            "bound": "mfma",
+            "achieved": round(dom_tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "dkdv_tflops": round(dk_tf, 2),
+        "hbm_algorithmic_GBps": round(bwd_bytes(w) / (ms * 1e-3) / 1e9, 1),
+        "outputs_finite": ok,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline and w.dtype == "bf16":
+        print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inputs_cpu, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,116 @@
+/*
+ * attn.h -- C ABI of libattn, scaled dot-product attention forward and
+ * backward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one head; every (batch, head) pair is independent, eulerpad
+ * "Attention backward" Problem 10 and the [batch, heads, seq, head_dim]
+ * layout of the step-by-step derivation's "Forward Pass"):
+ *
+ *   S = scale * Q K^T            Q: n x d, K: m x d      (mlgrind "Forward")
+ *   S_ij = -inf for j > i        only when causal; requires n == m
+ *   P = row softmax(S)           stable: the row max is subtracted
+ *   O = P V                      V: m x dv, O: n x dv
+ *   LSE_i = ln sum_j exp(S_ij)   natural log; P_ij = exp(S_ij - LSE_i)
+ *
+ * and its gradients for an upstream dO = dL/dO (n x dv)
+ * (mlgrind "Backward"; eulerpad Problems 2-6):
+ *
+ *   dV = P^T dO,  dP = dO V^T,  D_i = rowsum(dO o O)_i = rowsum(dP o P)_i,
+ *   dS = P o (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ * The backward recomputes P tile by tile from Q, K and LSE (mlgrind "Edge
+ * cases and conventions"); it never stores an n x m matrix.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are device pointers to contiguous row-major [B, H, rows, cols]
+ *    arrays: q [B,H,n,d], k [B,H,m,d], v [B,H,m,dv], o and dout [B,H,n,dv],
+ *    dq [B,H,n,d], dk [B,H,m,d], dv_out [B,H,m,dv], lse [B,H,n] (float32).
+ *  - dtype ATTN_F32: q, k, v, o, dout, dq, dk, dv_out are float32.
+ *    dtype ATTN_BF16: they are bfloat16; arithmetic accumulates in float32.
+ *  - Supported (d, dv): ATTN_BF16 {(64,64), (128,128), (128,64)};
+ *    ATTN_F32 any d, dv in 1..128.
+ *  - The caller owns every buffer.  The library allocates and frees nothing
+ *    and never synchronises: work is enqueued on `stream` (a hipStream_t;
+ *    NULL is the default stream) and the call returns.
+ *  - All validation happens before anything is enqueued; on an error return
+ *    nothing was launched and no output was touched.
+ *  - Sizes: B, H, n >= 0 (zero means an empty problem: a successful no-op,
+ *    except that attn_bwd with n == 0 zero-fills dk and dv_out); m >= 1 (a
+ *    softmax over no keys is undefined); d, dv >= 1.
+ *  - The library keeps no mutable global state; concurrent calls on
+ *    different streams with distinct outputs are safe.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, o, dout, dq, dk, dv_out.  lse is always float32. */
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Return codes. */
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,          /* null pointer, negative size, m < 1, d or dv < 1, non-finite scale */
+    ATTN_ECAUSAL_SHAPE = 2,   /* causal requested with n != m (mlgrind "Inputs") */
+    ATTN_EUNSUPPORTED = 3,    /* dtype or (d, dv) pair not built, or unknown flag bits */
+    ATTN_EWORKSPACE = 4,      /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
+    ATTN_EHIP = 5             /* the HIP runtime refused a launch */
+};
+
+/* attn_bwd flags.  Bits 0-3 choose how dQ is accumulated. */
+enum attn_bwd_flags {
+    ATTN_DQ_AUTO = 0,         /* library's choice (currently ATTN_DQ_SEPARATE) */
+    ATTN_DQ_SEPARATE = 1,     /* a second pass per query tile recomputes P and dS:
+                                 deterministic, no atomics */
+    /* Bits 8-10 restrict which kernels run (0 = all, in this order).  They
+       exist so that each kernel can be timed on its own; a caller wanting
+       gradients leaves them 0.  Later stages read what earlier ones wrote. */
+    ATTN_STAGE_PREPROCESS = 1 << 8,   /* D = rowsum(dO o O), LSE rescale */
+    ATTN_STAGE_DKDV = 1 << 9,         /* dK and dV */
+    ATTN_STAGE_DQ = 1 << 10           /* dQ */
+};
+
+/*
+ * Forward.  Writes o [B,H,n,dv] (dtype) and lse [B,H,n] (float32, natural
+ * log).  scale is the factor on Q K^T; pass 1/sqrt(d) for the usual choice
+ * (mlgrind "Forward": d = Q.shape[-1]).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int n, int m, int d, int dv, float scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for these sizes (a multiple of
+ * 256; zero for an empty problem).  Holds per-row D and rescaled LSE.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
+                                int flags);
+
+/*
+ * Backward.  Inputs q, k, v, o (the forward output), dout and lse (from
+ * attn_fwd on the same q, k, v, scale and causal).  Writes dq, dk, dv_out
+ * with the shapes of q, k and v.  workspace must be device memory of at
+ * least attn_bwd_workspace_bytes() bytes, 256-byte aligned; its contents on
+ * entry do not matter.  Output buffers must not overlap inputs.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv_out,
+             int B, int H, int n, int m, int d, int dv, float scale, int causal,
+             int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* attn_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

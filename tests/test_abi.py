@@ -1,0 +1,126 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (no compute call runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attn_bwd_amd as attn
+from transformer_attn_bwd_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    return attn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTED), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_version() >= 100
+    for code in range(6):
+        assert attn.status_str(code)
+    assert "unknown" in attn.status_str(99)
+
+
+def test_workspace_size(lib):
+    # two float32 arrays of B*H*round_up(n, 128) rows, rounded to 256 bytes
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128) == 2 * 64 * 4096 * 4
+    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64) == 2 * 128 * 4
+    assert attn.bwd_workspace_bytes(1, 1, 0, 5, 64, 64) == 0
+    assert attn.bwd_workspace_bytes(0, 4, 100, 5, 64, 64) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 96, 96, B.ATTN_BF16, 0) == 0  # unsupported
+
+
+NULL = None
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+
+
+def _fwd(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, causal=0,
+         dtype=B.ATTN_BF16, ptrs=None):
+    p = ptrs if ptrs is not None else [FAKE] * 5
+    return lib.attn_fwd(*p, B_, H, n, m, d, dv, scale, causal, dtype, NULL)
+
+
+def _bwd(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, causal=0, dtype=B.ATTN_BF16,
+         flags=0, ws=FAKE, ws_bytes=1 << 30, ptrs=None):
+    p = ptrs if ptrs is not None else [FAKE] * 9
+    return lib.attn_bwd(*p, B_, H, n, m, d, dv, scale, causal, dtype, flags, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), B.ATTN_EINVAL),
+    (dict(m=0), B.ATTN_EINVAL),
+    (dict(d=0), B.ATTN_EINVAL),
+    (dict(B_=-2), B.ATTN_EINVAL),
+    (dict(scale=float("nan")), B.ATTN_EINVAL),
+    (dict(scale=float("inf")), B.ATTN_EINVAL),
+    (dict(n=64, m=65, causal=1), B.ATTN_ECAUSAL_SHAPE),
+    (dict(d=96, dv=96), B.ATTN_EUNSUPPORTED),
+    (dict(d=64, dv=128), B.ATTN_EUNSUPPORTED),
+    (dict(dtype=7), B.ATTN_EUNSUPPORTED),
+    (dict(dtype=B.ATTN_F32, d=129), B.ATTN_EUNSUPPORTED),
+    (dict(n=(1 << 22) + 1, m=(1 << 22) + 1), B.ATTN_EUNSUPPORTED),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert _bwd(lib, **kw) == code
+
+
+def test_null_and_misaligned_pointers(lib):
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = NULL
+        assert _fwd(lib, ptrs=p) == B.ATTN_EINVAL
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = NULL
+        assert _bwd(lib, ptrs=p) == B.ATTN_EINVAL
+    odd = ctypes.c_void_p((1 << 20) + 2)   # not 16-byte aligned for bf16 rows
+    assert _fwd(lib, ptrs=[odd] + [FAKE] * 4) == B.ATTN_EINVAL
+
+
+def test_workspace_checks(lib):
+    need = lib.attn_bwd_workspace_bytes(1, 1, 64, 64, 64, 64, B.ATTN_BF16, 0)
+    assert _bwd(lib, ws=NULL) == B.ATTN_EWORKSPACE
+    assert _bwd(lib, ws_bytes=need - 1) == B.ATTN_EWORKSPACE
+    assert _bwd(lib, ws=ctypes.c_void_p((1 << 20) + 4), ws_bytes=need) == B.ATTN_EINVAL
+
+
+def test_unknown_flags(lib):
+    assert _bwd(lib, flags=1 << 20) == B.ATTN_EUNSUPPORTED
+    assert _bwd(lib, flags=7) == B.ATTN_EUNSUPPORTED
+
+
+def test_empty_problems_need_no_pointers(lib):
+    # B*H == 0: nothing to do, nothing launched, pointers may be NULL
+    assert _fwd(lib, B_=0, ptrs=[NULL] * 5) == B.ATTN_OK
+    assert _bwd(lib, B_=0, ptrs=[NULL] * 9, ws=NULL, ws_bytes=0) == B.ATTN_OK
+    # n == 0 forward: no query rows, nothing launched
+    assert _fwd(lib, n=0, ptrs=[NULL, FAKE, FAKE, NULL, NULL]) == B.ATTN_OK
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.fwd(q, q, q)

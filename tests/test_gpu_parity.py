@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path against the float64 oracle, element by element,
+on seeded inputs that span several tiles and end in ragged tails.
+
+Bar (per output tensor): bf16 max|err| / max|ref| <= 2e-2; float32 1e-5.
+LSE is compared absolutely (bf16 path 1e-3, float32 1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attn_bwd_amd as attn
+from transformer_attn_bwd_amd.workloads import WORKLOADS, Workload, make_inputs
+
+from gpu_util import TOL, compare_full, oracle_full, rel_err, run_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(name, B, H, n, m, d, dv, dtype, causal, seed, qk_mult=1.0, scale=None):
+    return Workload(name, B, H, n, m, d, dv, dtype, causal, seed, qk_mult, scale)
+
+
+def test_fp32_head_64():
+    """The single-head float32 workload, whole, against the oracle."""
+    w = WORKLOADS["head_64_fp32"]
+    say(f"case {w.describe()}")
+    inputs = make_inputs(w)
+    gpu = run_gpu(w, inputs)
+    compare_full(w, gpu, oracle_full(w, inputs))
+
+
+FP32_SHAPES = [
+    _w("f32_ragged_causal", 2, 3, 77, 77, 48, 48, "fp32", True, 11),
+    _w("f32_cross", 1, 2, 33, 130, 100, 20, "fp32", False, 12),
+    _w("f32_d128", 1, 1, 65, 65, 128, 128, "fp32", True, 13),
+    _w("f32_tiny", 1, 1, 1, 1, 1, 1, "fp32", False, 14),
+]
+
+
+@pytest.mark.parametrize("w", FP32_SHAPES, ids=lambda w: w.name)
+def test_fp32_shapes(w):
+    say(f"case {w.describe()}")
+    inputs = make_inputs(w)
+    compare_full(w, run_gpu(w, inputs), oracle_full(w, inputs))
+
+
+BF16_SHAPES = [
+    # several tiles in every direction, ragged tails, all three head-width pairs
+    _w("bf16_causal_300_d64", 1, 2, 300, 300, 64, 64, "bf16", True, 21),
+    _w("bf16_causal_257_d128", 2, 1, 257, 257, 128, 128, "bf16", True, 22),
+    _w("bf16_cross_200x333_d128_dv64", 1, 2, 200, 333, 128, 64, "bf16", False, 23, 3.0),
+    _w("bf16_cross_130x70_d128", 1, 1, 130, 70, 128, 128, "bf16", False, 24),
+    _w("bf16_noncausal_129x129_d64", 1, 3, 129, 129, 64, 64, "bf16", False, 25),
+    _w("bf16_causal_384_d128", 1, 1, 384, 384, 128, 128, "bf16", True, 26),
+    _w("bf16_single_key", 1, 1, 5, 1, 64, 64, "bf16", False, 27),
+    _w("bf16_single_row", 1, 1, 1, 1, 128, 64, "bf16", True, 28),
+    _w("bf16_cross_1x500_d128", 1, 1, 1, 500, 128, 128, "bf16", False, 29),
+    _w("bf16_stress_x30", 1, 1, 70, 90, 128, 64, "bf16", False, 30, 30.0 ** 0.5),
+]
+
+
+@pytest.mark.parametrize("w", BF16_SHAPES, ids=lambda w: w.name)
+def test_bf16_shapes(w):
+    say(f"case {w.describe()}")
+    inputs = make_inputs(w)
+    compare_full(w, run_gpu(w, inputs), oracle_full(w, inputs))
+
+
+@pytest.mark.parametrize("w", [BF16_SHAPES[0], BF16_SHAPES[2], BF16_SHAPES[5]], ids=lambda w: w.name)
+def test_bwd_alone_from_oracle_forward(w):
+    """The backward fed the oracle's O (rounded to bf16) and LSE, so that its
+    error is measured apart from the forward kernel's."""
+    say(f"case bwd-only {w.describe()}")
+    inputs = make_inputs(w, "cuda:0")
+    ref = oracle_full(w, inputs)
+    q, k, v, do = inputs
+    o = torch.from_numpy(ref["o"]).to(torch.bfloat16).cuda()
+    lse = torch.from_numpy(ref["lse"]).float().cuda()
+    dq, dk, dv = attn.bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal)
+    torch.cuda.synchronize()
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = rel_err(to64(got), ref[name])
+        say(f"  {name} {e:.3e}")
+        assert e <= TOL["bf16"], (name, e)
+
+
+def test_causal_1k_d64_whole_heads():
+    """The B=4, H=16, n=m=1024, d=64 causal workload: four heads compared
+    whole (every element) against the oracle."""
+    w = WORKLOADS["causal_1k_d64"]
+    say(f"case {w.describe()}")
+    inputs = make_inputs(w)
+    gpu = run_gpu(w, inputs)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (1, 7), (2, 3)]
+    for (b, h) in heads:
+        sub = [t[b:b + 1, h:h + 1] for t in inputs]
+        ref = oracle.attn_bwd(*(to64(t) for t in sub), scale=w.softmax_scale, causal=w.causal)
+        for name in ("o", "dq", "dk", "dv"):
+            e = rel_err(to64(gpu[name][b:b + 1, h:h + 1]), ref[name])
+            assert e <= TOL["bf16"], ((b, h), name, e)
+        assert np.max(np.abs(to64(gpu["lse"][b:b + 1, h:h + 1]) - ref["lse"])) <= 1e-3
+    say("  4 heads ok")
+
+
+def test_determinism_bitwise():
+    """No atomics: repeated backward calls give identical bits."""
+    w = _w("det", 2, 2, 320, 320, 128, 128, "bf16", True, 40)
+    inputs = make_inputs(w, "cuda:0")
+    q, k, v, do = inputs
+    o, lse = attn.fwd(q, k, v, causal=True)
+    a = attn.bwd(q, k, v, o, do, lse, causal=True)
+    b = attn.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_n_zero_gives_zero_key_gradients():
+    """No queries: dK and dV are empty sums, i.e. zero."""
+    dev = "cuda:0"
+    for dtype in (torch.bfloat16, torch.float32):
+        q = torch.empty(1, 2, 0, 64, dtype=dtype, device=dev)
+        k = torch.randn(1, 2, 70, 64, device=dev).to(dtype)
+        v = torch.randn(1, 2, 70, 64, device=dev).to(dtype)
+        o = torch.empty(1, 2, 0, 64, dtype=dtype, device=dev)
+        lse = torch.empty(1, 2, 0, dtype=torch.float32, device=dev)
+        dk = torch.full_like(k, 7.0)
+        dv = torch.full_like(v, 7.0)
+        attn.bwd(q, k, v, o, o, lse, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dk) == 0 and torch.count_nonzero(dv) == 0
+
+
+def test_error_leaves_outputs_untouched():
+    dev = "cuda:0"
+    w = _w("err", 1, 1, 64, 64, 64, 64, "bf16", False, 41)
+    q, k, v, do = make_inputs(w, dev)
+    o, lse = attn.fwd(q, k, v)
+    dq = torch.full_like(q, 3.0)
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(attn.AttnError) as ei:
+        attn.bwd(q, k, v, o, do, lse, workspace=small, dq=dq)
+    assert ei.value.status == 4
+    torch.cuda.synchronize()
+    assert torch.all(dq == 3.0)

@@ -1,0 +1,112 @@
+"""GPU checks at the full workload sizes, in the launch configuration the
+benchmark times.
+
+At these sizes the oracle evaluates sampled outputs one by one (query rows
+for O, LSE and dQ; key rows for dK and dV, which need the statistics of
+every query row) on sampled heads; properties that hold at any size
+(gradient invariants and the zero-Q/K closed forms) are checked on every
+head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_attn_bwd_amd.workloads import WORKLOADS, make_inputs
+
+from gpu_util import TOL, rel_err, run_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+BIG = ["causal_1k_d64", "causal_4k_d128", "causal_16k_d128", "cross_512x2048_d128_dv64"]
+
+
+def _sample(size, rng, extra=12):
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, size // 2, size - 2, size - 1]
+    rnd = rng.choice(size, size=min(extra, size), replace=False).tolist()
+    return sorted({i for i in fixed + rnd if 0 <= i < size})
+
+
+def _heads(w, rng):
+    hs = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(hs) < min(3, w.B * w.H):
+        hs.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    return sorted(hs)
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_workload_sampled_against_oracle(name):
+    w = WORKLOADS[name]
+    say(f"case sampled {w.describe()}")
+    gpu = run_gpu(w)
+    rng = np.random.default_rng(1234)
+    worst = {}
+    for (b, h) in _heads(w, rng):
+        Q, K, V, dO = (to64(gpu[t][b, h]) for t in ("q", "k", "v", "do"))
+        rows = _sample(w.n, rng)
+        cols = _sample(w.m, rng)
+        r = oracle.attn_rows(Q, K, V, dO, rows, scale=w.softmax_scale, causal=w.causal)
+        c = oracle.attn_cols(Q, K, V, dO, cols, scale=w.softmax_scale, causal=w.causal)
+        errs = {
+            "o": rel_err(to64(gpu["o"][b, h, rows]), r["o"]),
+            "dq": rel_err(to64(gpu["dq"][b, h, rows]), r["dq"]),
+            "dk": rel_err(to64(gpu["dk"][b, h, cols]), c["dk"]),
+            "dv": rel_err(to64(gpu["dv"][b, h, cols]), c["dv"]),
+            "lse_abs": float(np.max(np.abs(to64(gpu["lse"][b, h, rows]) - r["lse"]))),
+        }
+        say(f"  head {(b, h)}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()))
+        for key, val in errs.items():
+            worst[key] = max(worst.get(key, 0.0), val)
+    for key in ("o", "dq", "dk", "dv"):
+        assert worst[key] <= TOL["bf16"], (name, key, worst[key])
+    assert worst["lse_abs"] <= 1e-3
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_workload_invariants_every_head(name):
+    """Per head: sum_j dK_j = 0; sum_j dV_j = sum_i dO_i; <Q,dQ> = <K,dK>;
+    <V,dV> = <O,dO>.  Residuals are measured against the natural scale of
+    each identity (sums of magnitudes) and must be within 2e-2 of it."""
+    w = WORKLOADS[name]
+    say(f"case invariants {w.describe()}")
+    g = run_gpu(w)
+    f = {k_: g[k_].double() for k_ in ("q", "k", "v", "do", "o", "dq", "dk", "dv")}
+    checks = {
+        "sum_dk": ((f["dk"].sum(2)).abs().amax(-1), f["dk"].abs().sum(2).amax(-1)),
+        "sum_dv": ((f["dv"].sum(2) - f["do"].sum(2)).abs().amax(-1), f["dv"].abs().sum(2).amax(-1)),
+        "qdq_kdk": (((f["q"] * f["dq"]).sum((2, 3)) - (f["k"] * f["dk"]).sum((2, 3))).abs(),
+                    (f["q"] * f["dq"]).abs().sum((2, 3))),
+        "vdv_odo": (((f["v"] * f["dv"]).sum((2, 3)) - (f["o"] * f["do"]).sum((2, 3))).abs(),
+                    (f["v"] * f["dv"]).abs().sum((2, 3))),
+    }
+    for key, (resid, scale) in checks.items():
+        ratio = float((resid / scale.clamp_min(1e-30)).max())
+        say(f"  {key}: worst residual/scale {ratio:.3e}")
+        assert ratio <= 2e-2, (name, key, ratio)
+
+
+@pytest.mark.parametrize("name", ["causal_4k_d128", "cross_512x2048_d128_dv64", "causal_1k_d64"])
+def test_zero_qk_closed_form_full_size(name):
+    """Q = K = 0 at the full shape: P is uniform over the visible keys, so O
+    is the (prefix) mean of V's rows, dV is the matching weighted sum of dO,
+    and dQ = dK = 0 exactly (mlgrind 'Examples'; eulerpad P8)."""
+    w = WORKLOADS[name]
+    say(f"case closed form {w.describe()}")
+    q, k, v, do = make_inputs(w, "cuda:0")
+    q.zero_()
+    k.zero_()
+    g = run_gpu(w, (q, k, v, do))
+    V, dO = v.double(), do.double()
+    if w.causal:
+        cnt = torch.arange(1, w.n + 1, device=V.device, dtype=torch.float64)[:, None]
+        o_ref = V.cumsum(2) / cnt
+        dv_ref = (dO / cnt).flip(2).cumsum(2).flip(2)
+    else:
+        o_ref = V.mean(2, keepdim=True).expand(-1, -1, w.n, -1)
+        dv_ref = (dO.sum(2, keepdim=True) / w.m).expand(-1, -1, w.m, -1)
+    eo = float((g["o"].double() - o_ref).abs().max() / o_ref.abs().max())
+    ev = float((g["dv"].double() - dv_ref).abs().max() / dv_ref.abs().max())
+    say(f"  o {eo:.3e} dv {ev:.3e}")
+    assert eo <= TOL["bf16"] and ev <= TOL["bf16"]
+    assert torch.count_nonzero(g["dq"]) == 0
+    assert torch.count_nonzero(g["dk"]) == 0

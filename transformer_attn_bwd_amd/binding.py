@@ -1,0 +1,155 @@
+"""Thin ctypes binding over libattn.so.
+
+Argument marshalling only: PyTorch supplies device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.
+If the library has not been built the first call raises; there is no other
+implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+# Values of include/attn.h.
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
+ATTN_DQ_AUTO, ATTN_DQ_SEPARATE = 0, 1
+ATTN_STAGE_PREPROCESS, ATTN_STAGE_DKDV, ATTN_STAGE_DQ = 1 << 8, 1 << 9, 1 << 10
+DQ_MODES = {"auto": ATTN_DQ_AUTO, "separate": ATTN_DQ_SEPARATE}
+STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
+
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+            "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def load():
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m transformer_attn_bwd_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, I, vp]
+    lib.attn_fwd.restype = I
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.attn_bwd_workspace_bytes.restype = Z
+    lib.attn_bwd.argtypes = [vp] * 9 + [I] * 6 + [F, I, I, I, vp, Z, vp]
+    lib.attn_bwd.restype = I
+    lib.attn_status_str.argtypes = [I]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().attn_status_str(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, seq, dim]")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d [B, H, seq, dim]")
+    B, H, n, d = q.shape
+    m, dv = v.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, m, d) or tuple(v.shape[:2]) != (B, H):
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, H, n, m, d, dv
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """O [B,H,n,dv] (q's dtype) and LSE [B,H,n] (float32, natural log)."""
+    lib = load()
+    _check_dev(q, k, v)
+    B, H, n, m, d, dv = _shape(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    _check_dev(out, lse)
+    st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n, m, d, dv,
+                      float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto"):
+    code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
+    return int(load().attn_bwd_workspace_bytes(B, H, n, m, d, dv, code, DQ_MODES[dq_mode]))
+
+
+def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace=None,
+        dq=None, dk=None, dv=None, stages=None):
+    """(dq, dk, dv) with the shapes and dtype of (q, k, v).
+
+    ``stages`` (a subset of {"preprocess", "dkdv", "dq"}) restricts which
+    kernels run; it exists for timing single kernels.
+    """
+    lib = load()
+    _check_dev(q, k, v, o, do, lse)
+    B, H, n, m, d, dvw = _shape(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    flags = DQ_MODES[dq_mode]
+    if stages:
+        for s_ in stages:
+            flags |= STAGES[s_]
+    code = _dtype_code(q)
+    need = int(lib.attn_bwd_workspace_bytes(B, H, n, m, d, dvw, code, flags))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_dev(dq, dk, dv, workspace)
+    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                      _ptr(dk), _ptr(dv), B, H, n, m, d, dvw, float(scale), int(bool(causal)),
+                      code, flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                      _stream(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

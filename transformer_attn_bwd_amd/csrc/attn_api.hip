@@ -1,0 +1,175 @@
+// C ABI of libattn: argument validation, workspace carving and dispatch to
+// the gfx950 kernels.  Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+using attn::Problem;
+using attn::Workspace;
+
+constexpr int kMaxSeq = 1 << 22;          // n, m limit (grid y dimension and int math)
+constexpr int kStageMask = ATTN_STAGE_PREPROCESS | ATTN_STAGE_DKDV | ATTN_STAGE_DQ;
+constexpr int kDqModeMask = 0xF;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Sizes, dtype, head widths, causal shape and scale; shared by fwd and bwd.
+int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int causal, int dtype,
+                  Problem* out) {
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (B < 0 || H < 0 || n < 0 || m < 1 || d < 1 || dv < 1) return ATTN_EINVAL;
+    if (!isfinite(scale)) return ATTN_EINVAL;
+    if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
+    if (n > kMaxSeq || m > kMaxSeq) return ATTN_EUNSUPPORTED;
+    if (dtype == ATTN_BF16) {
+        const bool ok = (d == 64 && dv == 64) || (d == 128 && dv == 128) || (d == 128 && dv == 64);
+        if (!ok) return ATTN_EUNSUPPORTED;
+        if ((long)B * H > 0x7fffffffL) return ATTN_EUNSUPPORTED;
+    } else {
+        if (d > 128 || dv > 128) return ATTN_EUNSUPPORTED;
+        if ((long)B * H > 65535L) return ATTN_EUNSUPPORTED;
+    }
+    out->B = B;
+    out->H = H;
+    out->n = n;
+    out->m = m;
+    out->d = d;
+    out->dv = dv;
+    out->scale = scale;
+    out->causal = causal != 0;
+    out->dtype = dtype;
+    return ATTN_OK;
+}
+
+// A tensor with elements needs a non-null pointer aligned for the kernels'
+// vector accesses (16 bytes for bf16 rows, 4 bytes for float32).
+bool tensor_ok(const void* p, long elems, int dtype) {
+    if (elems == 0) return true;
+    if (p == nullptr) return false;
+    return aligned(p, dtype == ATTN_BF16 ? 16 : 4);
+}
+
+size_t workspace_bytes(const Problem& p) {
+    if (p.heads() == 0 || p.n == 0) return 0;
+    const size_t rows = (size_t)p.heads() * (size_t)attn::padded_rows(p.n);
+    return round_up(2 * rows * sizeof(float), 256);
+}
+
+int hip_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return 100; }
+
+const char* attn_status_str(int status) {
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument (null or misaligned pointer, bad size or scale)";
+    case ATTN_ECAUSAL_SHAPE: return "causal masking requires n == m";
+    case ATTN_EUNSUPPORTED: return "unsupported dtype, head widths, size or flags";
+    case ATTN_EWORKSPACE: return "workspace missing or too small";
+    case ATTN_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int n, int m, int d, int dv, float scale, int causal, int dtype, void* stream) {
+    Problem p;
+    int st = check_problem(B, H, n, m, d, dv, scale, causal, dtype, &p);
+    if (st != ATTN_OK) return st;
+    const long hq = p.heads() * (long)n, hk = p.heads() * (long)m;
+    if (!tensor_ok(q, hq * d, dtype) || !tensor_ok(k, hk * d, dtype) ||
+        !tensor_ok(v, hk * dv, dtype) || !tensor_ok(o, hq * dv, dtype) ||
+        !tensor_ok(lse, hq, ATTN_F32))
+        return ATTN_EINVAL;
+    if (hq == 0) return ATTN_OK;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    bool ok = dtype == ATTN_BF16
+                  ? attn::launch_fwd_bf16(p, q, k, v, o, lse, s)
+                  : attn::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v,
+                                         (float*)o, lse, s);
+    if (!ok) return ATTN_EUNSUPPORTED;
+    return hip_status();
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
+                                int flags) {
+    (void)flags;
+    Problem p;
+    if (check_problem(B, H, n, m, d, dv, 1.f, 0, dtype, &p) != ATTN_OK) return 0;
+    return workspace_bytes(p);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv_out, int B, int H, int n, int m,
+             int d, int dv, float scale, int causal, int dtype, int flags, void* workspace,
+             size_t workspace_bytes_given, void* stream) {
+    Problem p;
+    int st = check_problem(B, H, n, m, d, dv, scale, causal, dtype, &p);
+    if (st != ATTN_OK) return st;
+    if (flags & ~(kDqModeMask | kStageMask)) return ATTN_EUNSUPPORTED;
+    const int dq_mode = flags & kDqModeMask;
+    if (dq_mode != ATTN_DQ_AUTO && dq_mode != ATTN_DQ_SEPARATE) return ATTN_EUNSUPPORTED;
+    const long hq = p.heads() * (long)n, hk = p.heads() * (long)m;
+    if (!tensor_ok(q, hq * d, dtype) || !tensor_ok(k, hk * d, dtype) ||
+        !tensor_ok(v, hk * dv, dtype) || !tensor_ok(o, hq * dv, dtype) ||
+        !tensor_ok(dout, hq * dv, dtype) || !tensor_ok(lse, hq, ATTN_F32) ||
+        !tensor_ok(dq, hq * d, dtype) || !tensor_ok(dk, hk * d, dtype) ||
+        !tensor_ok(dv_out, hk * dv, dtype))
+        return ATTN_EINVAL;
+    const size_t need = workspace_bytes(p);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes_given < need) return ATTN_EWORKSPACE;
+        if (!aligned(workspace, 16)) return ATTN_EINVAL;
+    }
+    if (p.heads() == 0) return ATTN_OK;
+
+    int stages = flags & kStageMask;
+    if (stages == 0) stages = kStageMask;
+    Workspace w;
+    w.n_pad = attn::padded_rows(n);
+    w.lse2 = (float*)workspace;
+    w.D = w.lse2 + (size_t)p.heads() * (size_t)w.n_pad;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+
+    const bool bf = dtype == ATTN_BF16;
+    bool ok = true;
+    if (n > 0 && (stages & ATTN_STAGE_PREPROCESS)) {
+        ok = bf ? attn::launch_bwd_preprocess_bf16(p, o, dout, lse, w, s)
+                : attn::launch_bwd_preprocess_f32(p, (const float*)o, (const float*)dout, lse, w, s);
+        if (!ok) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (stages & ATTN_STAGE_DKDV) {
+        // With n == 0 the kernel visits no query tile and writes zeros.
+        ok = bf ? attn::launch_bwd_dkdv_bf16(p, q, k, v, dout, w, dk, dv_out, s)
+                : attn::launch_bwd_dkdv_f32(p, (const float*)q, (const float*)k, (const float*)v,
+                                            (const float*)dout, w, (float*)dk, (float*)dv_out, s);
+        if (!ok) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (n > 0 && (stages & ATTN_STAGE_DQ)) {
+        ok = bf ? attn::launch_bwd_dq_bf16(p, q, k, v, dout, w, dq, s)
+                : attn::launch_bwd_dq_f32(p, (const float*)q, (const float*)k, (const float*)v,
+                                          (const float*)dout, w, (float*)dq, s);
+        if (!ok) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,556 @@
+// Backward attention on bf16 MFMA (float32 accumulation), three kernels:
+//
+//  1. preprocess: D_i = rowsum(dO o O)_i, the cheap form of rowsum(dP o P)
+//     (step-by-step derivation, "Gradient of S"; mlgrind "Follow-up"), and
+//     LSE rescaled to base 2 so that P = exp2(S * scale * log2e - LSE2).
+//  2. dK/dV: one workgroup per 128 keys of a head (32 per wave); it walks
+//     the query tiles, recomputes S = Q K^T and P, and accumulates
+//     dV += P^T dO and dK += dS^T Q in registers (eulerpad P2, P6).
+//  3. dQ: one workgroup per 128 queries (32 per wave); it walks the key
+//     tiles, recomputes S^T, P^T, dP^T = V dO^T and dS^T, and accumulates
+//     dQ^T += K^T dS^T (eulerpad P5).  A separate pass costs three extra
+//     products per tile pair but needs no atomics and is deterministic.
+//
+// In kernel 2 the lane owns a key: the accumulator layout of S (rows =
+// queries, columns = keys) is exactly the A-operand layout P^T and dS^T
+// need (rows = keys, k = queries), so P and dS never leave registers; the
+// partners dO and Q are read from transposed LDS copies in the matching
+// row-of-C order.  Kernel 3 mirrors this with the lane owning a query.
+// The causal mask (S_ij = -inf for j > i, i.e. P_ij = 0, eulerpad P8) is
+// applied only in tiles that straddle the diagonal; tiles entirely above
+// it are never visited.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+// ---------------------------------------------------------------- preprocess
+
+template <int DV>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(
+    const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ lse2, float* __restrict__ Dw, int n, int n_pad, long total_rows) {
+    constexpr int LPR = DV / 8;        // lanes per row, 8 elements (16 bytes) each
+    constexpr int RPB = 256 / LPR;     // rows per block
+    const int tid = threadIdx.x;
+    const long row = (long)blockIdx.x * RPB + tid / LPR;
+    const int part = tid % LPR;
+    const bool valid_row = row < total_rows;
+    const long bh = valid_row ? row / n_pad : 0;
+    const int i = valid_row ? (int)(row % n_pad) : 0;
+    float acc = 0.f;
+    if (valid_row && i < n) {
+        const long off = (bh * (long)n + i) * DV + 8 * part;
+        bf16x8 a = gload_bf16x8(o + off);
+        bf16x8 b = gload_bf16x8(dout + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (valid_row && part == 0) {
+        lse2[row] = i < n ? lse[bh * (long)n + i] * kLog2e : 0.f;
+        Dw[row] = acc;
+    }
+}
+
+// ---------------------------------------------------------------- dK / dV
+
+template <int D, int DV>
+struct DkdvCfg {
+    static constexpr int BN = 128;           // keys per workgroup, 32 per wave
+    static constexpr int BM = 64;            // queries per step
+    static constexpr int LDQ = D + 8;        // row-major Q stride in LDS
+    static constexpr int LDO = DV + 8;       // row-major dO stride
+    static constexpr int LDT = BM + 4;       // transposed tiles: one row per column
+    static constexpr int Q_ITEMS = (BM / 4) * (D / 8);   // 4 rows x 8 columns each
+    static constexpr int O_ITEMS = (BM / 4) * (DV / 8);
+    static constexpr int Q_PER_T = (Q_ITEMS + 255) / 256;
+    static constexpr int O_PER_T = (O_ITEMS + 255) / 256;
+};
+
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ Dw, bf16* __restrict__ dk, bf16* __restrict__ dvo, int n, int m,
+    int n_pad, float scale, float c2) {
+    using C = DkdvCfg<D, DV>;
+    __shared__ __align__(16) bf16 sQ[2][C::BM * C::LDQ];
+    __shared__ __align__(16) bf16 sQT[2][D * C::LDT];
+    __shared__ __align__(16) bf16 sO[2][C::BM * C::LDO];
+    __shared__ __align__(16) bf16 sOT[2][DV * C::LDT];
+    __shared__ __align__(16) float sL[2][C::BM];
+    __shared__ __align__(16) float sD[2][C::BM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, li = lane & 31;
+    const long bh = blockIdx.x;
+    const int j0 = blockIdx.y * C::BN;
+    const int kw0 = j0 + 32 * wave;
+    const int myk = kw0 + li;
+
+    const bf16* qh = q + bh * (long)n * D;
+    const bf16* kh = k + bh * (long)m * D;
+    const bf16* vh = v + bh * (long)m * DV;
+    const bf16* oh = dout + bh * (long)n * DV;
+    const float* lh = lse2 + bh * (long)n_pad;
+    const float* dh = Dw + bh * (long)n_pad;
+
+    // This lane's key row: B operand of S = Q K^T and of dP = dO V^T.
+    bf16x8 kreg[D / 16], vreg[DV / 16];
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+        kreg[kc] = myk < m ? gload_bf16x8(kh + (long)myk * D + 16 * kc + 8 * g) : bf16x8{};
+#pragma unroll
+    for (int kc = 0; kc < DV / 16; ++kc)
+        vreg[kc] = myk < m ? gload_bf16x8(vh + (long)myk * DV + 16 * kc + 8 * g) : bf16x8{};
+
+    const int i_begin = CAUSAL ? (j0 / C::BM) * C::BM : 0;
+    const int i_end = (n + C::BM - 1) / C::BM * C::BM;
+    const int nsteps = (i_end - i_begin) / C::BM;
+
+    u32x4 qst[C::Q_PER_T][4], ost[C::O_PER_T][4];
+    float lst = 0.f, dst = 0.f;
+
+    auto fetch = [&](int i0) {
+#pragma unroll
+        for (int it = 0; it < C::Q_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::Q_ITEMS) {
+                const int rg = e / (D / 8), cg = e % (D / 8);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int row = i0 + 4 * rg + x;
+                    qst[it][x] = row < n ? gload16(qh + (long)row * D + 8 * cg) : u32x4{0, 0, 0, 0};
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::O_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::O_ITEMS) {
+                const int rg = e / (DV / 8), cg = e % (DV / 8);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int row = i0 + 4 * rg + x;
+                    ost[it][x] = row < n ? gload16(oh + (long)row * DV + 8 * cg) : u32x4{0, 0, 0, 0};
+                }
+            }
+        }
+        if (tid < C::BM) {
+            lst = lh[i0 + tid];
+            dst = dh[i0 + tid];
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < C::Q_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::Q_ITEMS) {
+                const int rg = e / (D / 8), cg = e % (D / 8);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    lds_write16(&sQ[buf][(4 * rg + x) * C::LDQ + 8 * cg], qst[it][x]);
+#pragma unroll
+                for (int y = 0; y < 8; ++y)
+                    lds_write8(&sQT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(qst[it], y));
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::O_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::O_ITEMS) {
+                const int rg = e / (DV / 8), cg = e % (DV / 8);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    lds_write16(&sO[buf][(4 * rg + x) * C::LDO + 8 * cg], ost[it][x]);
+#pragma unroll
+                for (int y = 0; y < 8; ++y)
+                    lds_write8(&sOT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(ost[it], y));
+            }
+        }
+        if (tid < C::BM) {
+            sL[buf][tid] = lst;
+            sD[buf][tid] = dst;
+        }
+    };
+
+    f32x16 accK[D / 32], accV[DV / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) accK[t] = zero16();
+#pragma unroll
+    for (int t = 0; t < DV / 32; ++t) accV[t] = zero16();
+
+    if (nsteps > 0) {
+        fetch(i_begin);
+        commit(0);
+    }
+    __syncthreads();
+
+    for (int step = 0; step < nsteps; ++step) {
+        const int buf = step & 1;
+        const int i0 = i_begin + step * C::BM;
+        const bool has_next = step + 1 < nsteps;
+        if (has_next) fetch(i0 + C::BM);
+
+        const bf16* Qs = sQ[buf];
+        const bf16* Os = sO[buf];
+        f32x16 S[2], dP[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            S[t] = zero16();
+            dP[t] = zero16();
+        }
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 a = lds_read8(Qs + (32 * t + li) * C::LDQ + 16 * kc + 8 * g);
+                S[t] = mfma32(a, kreg[kc], S[t]);
+            }
+        }
+#pragma unroll
+        for (int kc = 0; kc < DV / 16; ++kc) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 a = lds_read8(Os + (32 * t + li) * C::LDO + 16 * kc + 8 * g);
+                dP[t] = mfma32(a, vreg[kc], dP[t]);
+            }
+        }
+
+        const bool need_mask = CAUSAL && (i0 < j0 + C::BN - 1);
+        bf16x8 Pb[2][2], dSb[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            float p[16], ds[16];
+#pragma unroll
+            for (int vq = 0; vq < 4; ++vq) {
+                const int qoff = 32 * t + 8 * vq + 4 * g;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][qoff]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][qoff]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int vv = 4 * vq + r;
+                    float pv = fast_exp2(S[t][vv] * c2 - l4[r]);
+                    if (need_mask && myk > i0 + qoff + r) pv = 0.f;
+                    p[vv] = pv;
+                    ds[vv] = pv * (dP[t][vv] - d4[r]);
+                }
+            }
+            Pb[t][0] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            Pb[t][1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+            dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+        }
+
+        // dV (keys x dv) += P^T dO: A = P^T from registers, B = dO from sOT.
+#pragma unroll
+        for (int nt = 0; nt < DV / 32; ++nt) {
+            const bf16* row = sOT[buf] + (32 * nt + li) * C::LDT;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    accV[nt] = mfma32(Pb[t][c], read_rowc_pair(row, 32 * t + 16 * c, g), accV[nt]);
+            }
+        }
+        // dK (keys x d) += dS^T Q: A = dS^T from registers, B = Q from sQT.
+#pragma unroll
+        for (int nt = 0; nt < D / 32; ++nt) {
+            const bf16* row = sQT[buf] + (32 * nt + li) * C::LDT;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    accK[nt] = mfma32(dSb[t][c], read_rowc_pair(row, 32 * t + 16 * c, g), accK[nt]);
+            }
+        }
+
+        if (has_next) commit(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Accumulator slot vv of tile nt holds key kw0 + 8*(vv>>2) + 4g + (vv&3),
+    // column 32*nt + li.
+    bf16* dkh = dk + bh * (long)m * D;
+    bf16* dvh = dvo + bh * (long)m * DV;
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+        const int key = kw0 + 8 * (vv >> 2) + 4 * g + (vv & 3);
+        if (key < m) {
+#pragma unroll
+            for (int nt = 0; nt < D / 32; ++nt)
+                dkh[(long)key * D + 32 * nt + li] = (bf16)(accK[nt][vv] * scale);
+#pragma unroll
+            for (int nt = 0; nt < DV / 32; ++nt)
+                dvh[(long)key * DV + 32 * nt + li] = (bf16)accV[nt][vv];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D, int DV>
+struct DqCfg {
+    static constexpr int BM = 128;           // queries per workgroup, 32 per wave
+    static constexpr int BN = 64;            // keys per step
+    static constexpr int LDK = D + 8;
+    static constexpr int LDV = DV + 8;
+    static constexpr int LDT = BN + 4;
+    static constexpr int K_ITEMS = (BN / 4) * (D / 8);   // 4 rows x 8 columns each
+    static constexpr int V_ITEMS = BN * DV / 8;          // 16-byte chunks
+    static constexpr int K_PER_T = (K_ITEMS + 255) / 256;
+    static constexpr int V_PER_T = (V_ITEMS + 255) / 256;
+};
+
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ Dw, bf16* __restrict__ dq, int n, int m, int n_pad, float scale,
+    float c2) {
+    using C = DqCfg<D, DV>;
+    __shared__ __align__(16) bf16 sK[2][C::BN * C::LDK];
+    __shared__ __align__(16) bf16 sKT[2][D * C::LDT];
+    __shared__ __align__(16) bf16 sV[2][C::BN * C::LDV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, li = lane & 31;
+    const long bh = blockIdx.x;
+    const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+    const int i0 = qb * C::BM;
+    const int myq = i0 + 32 * wave + li;
+
+    const bf16* qh = q + bh * (long)n * D;
+    const bf16* kh = k + bh * (long)m * D;
+    const bf16* vh = v + bh * (long)m * DV;
+    const bf16* oh = dout + bh * (long)n * DV;
+
+    // This lane's query row: B operand of S^T = K Q^T and dP^T = V dO^T.
+    bf16x8 qreg[D / 16], oreg[DV / 16];
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+        qreg[kc] = myq < n ? gload_bf16x8(qh + (long)myq * D + 16 * kc + 8 * g) : bf16x8{};
+#pragma unroll
+    for (int kc = 0; kc < DV / 16; ++kc)
+        oreg[kc] = myq < n ? gload_bf16x8(oh + (long)myq * DV + 16 * kc + 8 * g) : bf16x8{};
+    const float l2 = lse2[bh * (long)n_pad + myq];
+    const float Dq = Dw[bh * (long)n_pad + myq];
+
+    const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
+    const int nsteps = (k_end + C::BN - 1) / C::BN;
+
+    u32x4 kst[C::K_PER_T][4], vst[C::V_PER_T];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int it = 0; it < C::K_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::K_ITEMS) {
+                const int rg = e / (D / 8), cg = e % (D / 8);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int key = k0 + 4 * rg + x;
+                    kst[it][x] = key < m ? gload16(kh + (long)key * D + 8 * cg) : u32x4{0, 0, 0, 0};
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::V_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::V_ITEMS) {
+                const int r = e / (DV / 8), cg = e % (DV / 8);
+                const int key = k0 + r;
+                vst[it] = key < m ? gload16(vh + (long)key * DV + 8 * cg) : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < C::K_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::K_ITEMS) {
+                const int rg = e / (D / 8), cg = e % (D / 8);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    lds_write16(&sK[buf][(4 * rg + x) * C::LDK + 8 * cg], kst[it][x]);
+#pragma unroll
+                for (int y = 0; y < 8; ++y)
+                    lds_write8(&sKT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(kst[it], y));
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::V_PER_T; ++it) {
+            const int e = tid + it * 256;
+            if (e < C::V_ITEMS) {
+                const int r = e / (DV / 8), cg = e % (DV / 8);
+                lds_write16(&sV[buf][r * C::LDV + 8 * cg], vst[it]);
+            }
+        }
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = zero16();
+
+    if (nsteps > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+
+    for (int step = 0; step < nsteps; ++step) {
+        const int buf = step & 1;
+        const int k0 = step * C::BN;
+        const bool has_next = step + 1 < nsteps;
+        if (has_next) fetch(k0 + C::BN);
+
+        const bf16* Ks = sK[buf];
+        const bf16* Vs = sV[buf];
+        f32x16 S[2], dP[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            S[t] = zero16();
+            dP[t] = zero16();
+        }
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 a = lds_read8(Ks + (32 * t + li) * C::LDK + 16 * kc + 8 * g);
+                S[t] = mfma32(a, qreg[kc], S[t]);
+            }
+        }
+#pragma unroll
+        for (int kc = 0; kc < DV / 16; ++kc) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 a = lds_read8(Vs + (32 * t + li) * C::LDV + 16 * kc + 8 * g);
+                dP[t] = mfma32(a, oreg[kc], dP[t]);
+            }
+        }
+
+        const bool need_mask = (CAUSAL && k0 + C::BN - 1 > i0) || (k0 + C::BN > m);
+        bf16x8 dSb[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            float ds[16];
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                float pv = fast_exp2(S[t][vv] * c2 - l2);
+                if (need_mask) {
+                    const int key = k0 + 32 * t + 8 * (vv >> 2) + 4 * g + (vv & 3);
+                    if (key >= m || (CAUSAL && key > myq)) pv = 0.f;
+                }
+                ds[vv] = pv * (dP[t][vv] - Dq);
+            }
+            dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+        }
+
+        // dQ^T (d x queries) += K^T dS^T: A = K^T from sKT, B = dS^T from registers.
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+            const bf16* row = sKT[buf] + (32 * mt + li) * C::LDT;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    acc[mt] = mfma32(read_rowc_pair(row, 32 * t + 16 * c, g), dSb[t][c], acc[mt]);
+            }
+        }
+
+        if (has_next) commit(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Accumulator slot vv of tile mt holds column d = 32*mt + 8*(vv>>2) + 4g + (vv&3)
+    // of this lane's query.
+    if (myq < n) {
+        bf16* qrow = dq + (bh * (long)n + myq) * D;
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+            for (int vq = 0; vq < 4; ++vq) {
+                bf16x4 w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[mt][4 * vq + r] * scale);
+                *reinterpret_cast<bf16x4*>(qrow + 32 * mt + 8 * vq + 4 * g) = w;
+            }
+        }
+    }
+}
+
+template <int DV>
+void launch_pre(const Problem& p, const void* o, const void* dout, const float* lse,
+                const Workspace& w, hipStream_t s) {
+    constexpr int RPB = 256 / (DV / 8);
+    const long total = p.heads() * (long)w.n_pad;
+    const unsigned blocks = (unsigned)((total + RPB - 1) / RPB);
+    bwd_preprocess_kernel<DV><<<blocks, 256, 0, s>>>((const bf16*)o, (const bf16*)dout, lse,
+                                                     w.lse2, w.D, p.n, w.n_pad, total);
+}
+
+template <int D, int DV>
+void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
+                 const void* dout, const Workspace& w, void* dk, void* dv, hipStream_t s) {
+    using C = DkdvCfg<D, DV>;
+    dim3 grid((unsigned)p.heads(), (unsigned)((p.m + C::BN - 1) / C::BN));
+    const float c2 = p.scale * kLog2e;
+    if (p.causal)
+        bwd_dkdv_kernel<D, DV, true><<<grid, 256, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
+            (bf16*)dk, (bf16*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+    else
+        bwd_dkdv_kernel<D, DV, false><<<grid, 256, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
+            (bf16*)dk, (bf16*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+}
+
+template <int D, int DV>
+void launch_dq(const Problem& p, const void* q, const void* k, const void* v, const void* dout,
+               const Workspace& w, void* dq, hipStream_t s) {
+    using C = DqCfg<D, DV>;
+    dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
+    const float c2 = p.scale * kLog2e;
+    if (p.causal)
+        bwd_dq_kernel<D, DV, true><<<grid, 256, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
+            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+    else
+        bwd_dq_kernel<D, DV, false><<<grid, 256, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
+            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+}
+
+}  // namespace
+
+bool launch_bwd_preprocess_bf16(const Problem& p, const void* o, const void* dout,
+                                const float* lse, const Workspace& w, hipStream_t s) {
+    if (p.dv == 64) launch_pre<64>(p, o, dout, lse, w, s);
+    else if (p.dv == 128) launch_pre<128>(p, o, dout, lse, w, s);
+    else return false;
+    return true;
+}
+
+bool launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                          const void* dout, const Workspace& w, void* dk, void* dv,
+                          hipStream_t s) {
+    if (p.d == 64 && p.dv == 64) launch_dkdv<64, 64>(p, q, k, v, dout, w, dk, dv, s);
+    else if (p.d == 128 && p.dv == 128) launch_dkdv<128, 128>(p, q, k, v, dout, w, dk, dv, s);
+    else if (p.d == 128 && p.dv == 64) launch_dkdv<128, 64>(p, q, k, v, dout, w, dk, dv, s);
+    else return false;
+    return true;
+}
+
+bool launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                        const void* dout, const Workspace& w, void* dq, hipStream_t s) {
+    if (p.d == 64 && p.dv == 64) launch_dq<64, 64>(p, q, k, v, dout, w, dq, s);
+    else if (p.d == 128 && p.dv == 128) launch_dq<128, 128>(p, q, k, v, dout, w, dq, s);
+    else if (p.d == 128 && p.dv == 64) launch_dq<128, 64>(p, q, k, v, dout, w, dq, s);
+    else return false;
+    return true;
+}
+
+}  // namespace attn

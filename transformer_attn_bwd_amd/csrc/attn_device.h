@@ -1,0 +1,115 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, the 32x32x16 bf16 MFMA, bf16 packing and the operand
+// layouts the kernels rely on.
+//
+// MFMA v_mfma_f32_32x32x16_bf16, one wave of 64 lanes, lane l, g = l >> 5,
+// li = l & 31:
+//   A (32 x 16, M x K): lane l holds row li, eight k values in slots s=0..7
+//   B (16 x 32, K x N): lane l holds column li, eight k values in slots s
+//   C (32 x 32, M x N): lane l holds column li, rows 8*(v>>2) + 4*g + (v&3)
+//                       in accumulator slots v = 0..15
+// A and B place a given k at the same (g, s) position, so any assignment of
+// logical k values to (g, s) gives the same product as long as both
+// operands use it.  Two assignments are used:
+//   natural:   k = 8*g + s                 (operands read from memory)
+//   row-of-C:  k = 8*(s>>2) + 4*g + (s&3)  within a 16-row half c of a C
+//              tile, i.e. C slots v = 8*c + s reused as an operand.  The
+//              partner operand then reads rows 4g..4g+3 and 8+4g..8+4g+3,
+//              two runs of four, which is what read_rowc_pair() fetches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Eight fp32 values -> eight bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                        float a5, float a6, float a7) {
+    bf16x8 r;
+    r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+    r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+    return r;
+}
+
+// Accumulator slots 8c..8c+7 of a C tile as a bf16 operand (row-of-C order).
+__device__ __forceinline__ bf16x8 c_half_to_bf16(const f32x16& x, int c) {
+    return pack8(x[8 * c + 0], x[8 * c + 1], x[8 * c + 2], x[8 * c + 3],
+                 x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]);
+}
+
+// The partner of a row-of-C operand, from a transposed LDS tile whose row
+// `p` (pointer to its first element) lists the C-tile rows contiguously:
+// elements base+4g..base+4g+3 and base+8+4g..base+8+4g+3.
+__device__ __forceinline__ bf16x8 read_rowc_pair(const bf16* p, int base, int g) {
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + base + 4 * g);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + base + 8 + 4 * g);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 gload_bf16x8(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void lds_write16(bf16* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ void lds_write8(bf16* p, u32x2 v) {
+    *reinterpret_cast<u32x2*>(p) = v;
+}
+
+// Given four rows of eight bf16 (one 16-byte chunk each, rows r..r+3 of a
+// tile, columns c..c+7), form column c+y of those four rows as four bf16
+// packed in 8 bytes: the transposed piece written to a [col][row] LDS tile.
+__device__ __forceinline__ u32x2 column4(const u32x4 (&rows)[4], int y) {
+    const int w = y >> 1;
+    u32x2 r;
+    if (y & 1) {
+        r[0] = (rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u);
+        r[1] = (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u);
+    } else {
+        r[0] = (rows[0][w] & 0xffffu) | (rows[1][w] << 16);
+        r[1] = (rows[2][w] & 0xffffu) | (rows[3][w] << 16);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor_lane32(float x) {
+    // exchange with the lane 32 positions away (the other half of the wave)
+    return __shfl_xor(x, 32, 64);
+}
+
+}  // namespace attn
