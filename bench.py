@@ -79,7 +79,8 @@ def cpu_baseline(w, inputs, heads_wanted):
     import numpy as np
     import oracle
     threads = oracle.num_threads()
-    nh = max(1, min(heads_wanted or threads, w.B * w.H))
+    # about 20 s of float64 work at the headline size: four heads per thread
+    nh = max(1, min(heads_wanted or 4 * threads, w.B * w.H))
     q, k, v, do = (t.reshape(w.B * w.H, *t.shape[2:])[:nh].double().numpy() for t in inputs)
     q, k, v, do = (np.ascontiguousarray(x[None]) for x in (q, k, v, do))
     t0 = time.perf_counter()
@@ -103,6 +104,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (a known-traffic "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,6 +123,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"bench: {w.describe()}", file=sys.stderr, flush=True)
+
+    if args.copy_probe_mib > 0:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     inputs_cpu = make_inputs(w, "cpu")
     q, k, v, do = (t.to(dev) for t in inputs_cpu)

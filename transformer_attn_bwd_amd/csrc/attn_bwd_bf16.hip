@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (valid_row && part == 0) {
-        lse2[row] = i < n ? lse[bh * (long)n + i] * kLog2e : 0.f;
+        lse2[row] = i < n ? lse[bh * (long)n + i] * kLog2e : INFINITY;
         Dw[row] = acc;
     }
 }
@@ -61,28 +61,20 @@ template <int D, int DV>
 struct DkdvCfg {
     static constexpr int BN = 128;           // keys per workgroup, 32 per wave
     static constexpr int BM = 64;            // queries per step
-    static constexpr int LDQ = D + 8;        // row-major Q stride in LDS
-    static constexpr int LDO = DV + 8;       // row-major dO stride
-    static constexpr int LDT = BM + 4;       // transposed tiles: one row per column
-    static constexpr int Q_ITEMS = (BM / 4) * (D / 8);   // 4 rows x 8 columns each
-    static constexpr int O_ITEMS = (BM / 4) * (DV / 8);
-    static constexpr int Q_PER_T = (Q_ITEMS + 255) / 256;
-    static constexpr int O_PER_T = (O_ITEMS + 255) / 256;
 };
 
 template <int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ Dw, bf16* __restrict__ dk, bf16* __restrict__ dvo, int n, int m,
     int n_pad, float scale, float c2) {
     using C = DkdvCfg<D, DV>;
-    __shared__ __align__(16) bf16 sQ[2][C::BM * C::LDQ];
-    __shared__ __align__(16) bf16 sQT[2][D * C::LDT];
-    __shared__ __align__(16) bf16 sO[2][C::BM * C::LDO];
-    __shared__ __align__(16) bf16 sOT[2][DV * C::LDT];
-    __shared__ __align__(16) float sL[2][C::BM];
-    __shared__ __align__(16) float sD[2][C::BM];
+    constexpr int BM = C::BM;
+    __shared__ __align__(1024) bf16 sQ[2][BM * D];
+    __shared__ __align__(1024) bf16 sO[2][BM * DV];
+    __shared__ __align__(256) float sL[2][BM];
+    __shared__ __align__(256) float sD[2][BM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -107,74 +99,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int kc = 0; kc < DV / 16; ++kc)
         vreg[kc] = myk < m ? gload_bf16x8(vh + (long)myk * DV + 16 * kc + 8 * g) : bf16x8{};
 
-    const int i_begin = CAUSAL ? (j0 / C::BM) * C::BM : 0;
-    const int i_end = (n + C::BM - 1) / C::BM * C::BM;
-    const int nsteps = (i_end - i_begin) / C::BM;
+    const int i_begin = CAUSAL ? (j0 / BM) * BM : 0;
+    const int i_end = (n + BM - 1) / BM * BM;
+    const int nsteps = (i_end - i_begin) / BM;
 
-    u32x4 qst[C::Q_PER_T][4], ost[C::O_PER_T][4];
-    float lst = 0.f, dst = 0.f;
-
-    auto fetch = [&](int i0) {
-#pragma unroll
-        for (int it = 0; it < C::Q_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::Q_ITEMS) {
-                const int rg = e / (D / 8), cg = e % (D / 8);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int row = i0 + 4 * rg + x;
-                    qst[it][x] = row < n ? gload16(qh + (long)row * D + 8 * cg) : u32x4{0, 0, 0, 0};
-                }
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::O_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::O_ITEMS) {
-                const int rg = e / (DV / 8), cg = e % (DV / 8);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int row = i0 + 4 * rg + x;
-                    ost[it][x] = row < n ? gload16(oh + (long)row * DV + 8 * cg) : u32x4{0, 0, 0, 0};
-                }
-            }
-        }
-        if (tid < C::BM) {
-            lst = lh[i0 + tid];
-            dst = dh[i0 + tid];
-        }
-    };
-    auto commit = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < C::Q_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::Q_ITEMS) {
-                const int rg = e / (D / 8), cg = e % (D / 8);
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    lds_write16(&sQ[buf][(4 * rg + x) * C::LDQ + 8 * cg], qst[it][x]);
-#pragma unroll
-                for (int y = 0; y < 8; ++y)
-                    lds_write8(&sQT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(qst[it], y));
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::O_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::O_ITEMS) {
-                const int rg = e / (DV / 8), cg = e % (DV / 8);
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    lds_write16(&sO[buf][(4 * rg + x) * C::LDO + 8 * cg], ost[it][x]);
-#pragma unroll
-                for (int y = 0; y < 8; ++y)
-                    lds_write8(&sOT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(ost[it], y));
-            }
-        }
-        if (tid < C::BM) {
-            sL[buf][tid] = lst;
-            sD[buf][tid] = dst;
-        }
+    // Stage query tile i0 into buffer buf: Q and dO rows (rows past n repeat
+    // row n-1; their LSE2 is +inf, so P = 0 and they contribute nothing),
+    // and the per-row LSE2 and D.
+    auto stage = [&](int buf, int i0) {
+        tile_load_async<D, BM>(sQ[buf], qh, i0, n, wave, 4, lane);
+        tile_load_async<DV, BM>(sO[buf], oh, i0, n, wave, 4, lane);
+        if (wave == 0)
+            __builtin_amdgcn_global_load_lds(lh + i0 + lane, (ATTN_LDS void*)sL[buf], 4, 0, 0);
+        else if (wave == 1)
+            __builtin_amdgcn_global_load_lds(dh + i0 + lane, (ATTN_LDS void*)sD[buf], 4, 0, 0);
     };
 
     f32x16 accK[D / 32], accV[DV / 32];
@@ -183,92 +121,129 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int t = 0; t < DV / 32; ++t) accV[t] = zero16();
 
-    if (nsteps > 0) {
-        fetch(i_begin);
-        commit(0);
-    }
+    if (nsteps > 0) stage(0, i_begin);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int step = 0; step < nsteps; ++step) {
         const int buf = step & 1;
-        const int i0 = i_begin + step * C::BM;
-        const bool has_next = step + 1 < nsteps;
-        if (has_next) fetch(i0 + C::BM);
+        const int i0 = i_begin + step * BM;
+        if (step + 1 < nsteps) stage(buf ^ 1, i0 + BM);
 
         const bf16* Qs = sQ[buf];
         const bf16* Os = sO[buf];
-        f32x16 S[2], dP[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            S[t] = zero16();
-            dP[t] = zero16();
-        }
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 a = lds_read8(Qs + (32 * t + li) * C::LDQ + 16 * kc + 8 * g);
-                S[t] = mfma32(a, kreg[kc], S[t]);
-            }
-        }
-#pragma unroll
-        for (int kc = 0; kc < DV / 16; ++kc) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 a = lds_read8(Os + (32 * t + li) * C::LDO + 16 * kc + 8 * g);
-                dP[t] = mfma32(a, vreg[kc], dP[t]);
-            }
-        }
-
+        const float* Ls = sL[buf];
+        const float* Dsm = sD[buf];
         const bool need_mask = CAUSAL && (i0 < j0 + C::BN - 1);
+
+        // The step is a fixed sequence of NA + NC products, issued one per
+        // slot in this order:
+        //   A ops (per query half t): S[t] += Q_t K^T (D/16), dP[t] += dO_t V^T (DV/16)
+        //   C ops (per t, c):         dV += P^T dO (DV/32), dK += dS^T Q (D/32)
+        // Each product's LDS operand is fetched PD slots ahead, and the
+        // softmax of one half is spread over the slots of the other half's
+        // products, so that the matrix cores, the LDS and the vector ALUs
+        // work at the same time.  Slots are fenced with sched_barrier so the
+        // compiler keeps this order.
+        constexpr int KA = D / 16, KB = DV / 16;
+        constexpr int NAT = KA + KB, NA = 2 * NAT;
+        constexpr int NCT = 2 * (DV / 32 + D / 32), NC = 2 * NCT;
+        constexpr int NOPS = NA + NC;
+        constexpr int PD = 4;
+
+        auto load_op = [&](auto oc_) -> bf16x8 {
+            constexpr int o = decltype(oc_)::value;
+            if constexpr (o < NA) {
+                constexpr int t = o / NAT, r = o % NAT;
+                if constexpr (r < KA) return tile_read8<D>(Qs, 32 * t + li, 2 * r + g);
+                else return tile_read8<DV>(Os, 32 * t + li, 2 * (r - KA) + g);
+            } else {
+                constexpr int oc = o - NA;
+                constexpr int t = oc / NCT, rc = oc % NCT;
+                constexpr int c = rc / (DV / 32 + D / 32), x = rc % (DV / 32 + D / 32);
+                if constexpr (x < DV / 32) return tile_read_tr<DV>(Os, 32 * t + 16 * c, 32 * x, lane);
+                else return tile_read_tr<D>(Qs, 32 * t + 16 * c, 32 * (x - DV / 32), lane);
+            }
+        };
+
+        f32x16 S[2], dP[2];
         bf16x8 Pb[2][2], dSb[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            float p[16], ds[16];
+        f32x4 l4[4], d4[4];
+        float p[16], ds[16];
+
+        auto load_stats = [&](int t) {
 #pragma unroll
             for (int vq = 0; vq < 4; ++vq) {
                 const int qoff = 32 * t + 8 * vq + 4 * g;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][qoff]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][qoff]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int vv = 4 * vq + r;
-                    float pv = fast_exp2(S[t][vv] * c2 - l4[r]);
-                    if (need_mask && myk > i0 + qoff + r) pv = 0.f;
-                    p[vv] = pv;
-                    ds[vv] = pv * (dP[t][vv] - d4[r]);
-                }
+                l4[vq] = *reinterpret_cast<const f32x4*>(Ls + qoff);
+                d4[vq] = *reinterpret_cast<const f32x4*>(Dsm + qoff);
             }
+        };
+        // Softmax of half T, rows 4VQ..4VQ+3 of the accumulator slots.
+        auto softmax_part = [&](auto t_, auto vq_) {
+            constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
+            const int qoff = 32 * t + 8 * vq + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int vv = 4 * vq + r;
+                float pv = fast_exp2(S[t][vv] * c2 - l4[vq][r]);
+                pv = (need_mask && myk > i0 + qoff + r) ? 0.f : pv;
+                p[vv] = pv;
+                ds[vv] = pv * (dP[t][vv] - d4[vq][r]);
+            }
+        };
+        auto pack_half = [&](auto t_) {
+            constexpr int t = decltype(t_)::value;
             Pb[t][0] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
             Pb[t][1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
             dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
             dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-        }
+        };
 
-        // dV (keys x dv) += P^T dO: A = P^T from registers, B = dO from sOT.
-#pragma unroll
-        for (int nt = 0; nt < DV / 32; ++nt) {
-            const bf16* row = sOT[buf] + (32 * nt + li) * C::LDT;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    accV[nt] = mfma32(Pb[t][c], read_rowc_pair(row, 32 * t + 16 * c, g), accV[nt]);
-            }
-        }
-        // dK (keys x d) += dS^T Q: A = dS^T from registers, B = Q from sQT.
-#pragma unroll
-        for (int nt = 0; nt < D / 32; ++nt) {
-            const bf16* row = sQT[buf] + (32 * nt + li) * C::LDT;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    accK[nt] = mfma32(dSb[t][c], read_rowc_pair(row, 32 * t + 16 * c, g), accK[nt]);
-            }
-        }
+        // Slots at which the softmax pieces of each half run: half 0 during
+        // the A ops of half 1 (after its inputs have had time to land), half
+        // 1 during the first C ops.
+        constexpr int SM0 = NAT + 2;
+        constexpr int SM1 = NA + 1;
 
-        if (has_next) commit(buf ^ 1);
+        bf16x8 fr[PD];
+        static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
+        load_stats(0);
+        __builtin_amdgcn_sched_barrier(0);
+
+        static_for<NOPS>([&](auto o_) {
+            constexpr int o = decltype(o_)::value;
+            const bf16x8 cur = fr[o % PD];
+            if constexpr (o + PD < NOPS)
+                fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
+            if constexpr (o < NA) {
+                constexpr int t = o / NAT, r = o % NAT;
+                if constexpr (r == 0) {
+                    S[t] = zero16();
+                    dP[t] = zero16();
+                }
+                if constexpr (r < KA) S[t] = mfma32(cur, kreg[r], S[t]);
+                else dP[t] = mfma32(cur, vreg[r - KA], dP[t]);
+            } else {
+                constexpr int oc = o - NA;
+                constexpr int t = oc / NCT, rc = oc % NCT;
+                constexpr int c = rc / (DV / 32 + D / 32), x = rc % (DV / 32 + D / 32);
+                if constexpr (x < DV / 32) accV[x] = mfma32(Pb[t][c], cur, accV[x]);
+                else accK[x - DV / 32] = mfma32(dSb[t][c], cur, accK[x - DV / 32]);
+            }
+            if constexpr (o >= SM0 && o < SM0 + 4)
+                softmax_part(std::integral_constant<int, 0>{}, std::integral_constant<int, o - SM0>{});
+            if constexpr (o == SM0 + 4) {
+                pack_half(std::integral_constant<int, 0>{});
+                load_stats(1);
+            }
+            if constexpr (o >= SM1 && o < SM1 + 4)
+                softmax_part(std::integral_constant<int, 1>{}, std::integral_constant<int, o - SM1>{});
+            if constexpr (o == SM1 + 4) pack_half(std::integral_constant<int, 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 

@@ -21,6 +21,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace attn {
 
 typedef __bf16 bf16;
@@ -30,6 +33,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0..N-1, so that every
+// index inside f is a compile-time constant (register arrays stay arrays).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(static_cast<F&&>(f), std::make_integer_sequence<int, N>{});
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -106,6 +120,77 @@ __device__ __forceinline__ u32x2 column4(const u32x4 (&rows)[4], int y) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define ATTN_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------------------
+// Swizzled row-major LDS tiles filled straight from global memory.
+//
+// A tile of ROWS x C bf16 is stored row-major in 16-byte chunks; chunk c of
+// row r sits in slot c ^ swz(r).  The swizzle makes both access patterns the
+// kernels use free of bank conflicts (64 banks x 4 bytes):
+//  - operand reads of 16 bytes by 16 lanes on 16 consecutive rows, same chunk;
+//  - transposing reads of 8 bytes by 32 lanes on 4 rows x 4 chunks.
+// Tiles are written with global_load_lds_dwordx4: one wave instruction moves
+// 1 KB, lane L filling the L-th 16-byte slot of that kilobyte, so the
+// swizzle is applied on the global side by choosing which chunk each lane
+// fetches.
+template <int C>
+struct SwzTile {
+    static constexpr int CPR = C / 8;                    // 16-byte chunks per row
+    static_assert(CPR == 8 || CPR == 16, "tile widths of 64 or 128 bf16");
+    __device__ static __forceinline__ int swz(int r) {
+        if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+        else return (((r >> 1) & 1) << 2) ^ ((r >> 2) & 3);
+    }
+    // element offset of chunk c (8 bf16) of row r
+    __device__ static __forceinline__ int off(int r, int c) { return r * C + 8 * (c ^ swz(r)); }
+};
+
+// Fill `rows` rows of a swizzled tile from global rows row0.. of a [*, C]
+// row-major bf16 matrix; rows at or past `valid` read row valid-1 instead
+// (callers neutralise them).  Called by `nw` waves, wave `w`.
+template <int C, int ROWS>
+__device__ __forceinline__ void tile_load_async(bf16* lds_tile, const bf16* g, int row0,
+                                                int valid, int w, int nw, int lane) {
+    using T = SwzTile<C>;
+    constexpr int INSTS = ROWS * T::CPR / 64;
+    for (int ii = w; ii < INSTS; ii += nw) {
+        const int p = ii * 64 + lane;
+        const int r = p / T::CPR;
+        const int s = p % T::CPR;
+        int grow = row0 + r;
+        grow = grow < valid ? grow : valid - 1;
+        const bf16* src = g + (long)grow * C + 8 * (s ^ T::swz(r));
+        __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + ii * 512), 16, 0, 0);
+    }
+}
+
+// 8 contiguous bf16 of row r, chunk c (an MFMA operand in natural k order).
+template <int C>
+__device__ __forceinline__ bf16x8 tile_read8(const bf16* lds_tile, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(lds_tile + SwzTile<C>::off(r, c));
+}
+
+// Transposing read: the partner of a row-of-C operand.  Lane l (g = l>>5)
+// receives column n0 + (l & 31) of rows base+4g..base+4g+3 (slots 0-3) and
+// base+8+4g..base+8+4g+3 (slots 4-7), from a swizzled row-major tile.
+// ds_read_b64_tr_b16 works on blocks of 16 lanes: lane i of a block gets
+// element (i & 3) of the 8-byte rows addressed by lanes 4e+(i>>2), e=0..3.
+template <int C>
+__device__ __forceinline__ bf16x8 tile_read_tr(const bf16* lds_tile, int base, int n0, int lane) {
+    const int blk = lane >> 4, j = lane & 15;
+    const int g = blk >> 1;
+    const int col = n0 + 16 * (blk & 1) + 4 * (j & 3);
+    const int r = base + 4 * g + (j >> 2);
+    const int o0 = SwzTile<C>::off(r, col >> 3) + (col & 7);
+    const int o1 = SwzTile<C>::off(r + 8, col >> 3) + (col & 7);
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(lds_tile + o0));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(lds_tile + o1));
+    i16x4 both[2] = {lo, hi};
+    return *reinterpret_cast<bf16x8*>(both);
+}
 
 __device__ __forceinline__ float xor_lane32(float x) {
     // exchange with the lane 32 positions away (the other half of the wave)
