@@ -25,6 +25,9 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # keep hipcc from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results and accumulators in architectural VGPRs: the kernels need
+    # their softmax inputs in VGPRs anyway, and this avoids AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

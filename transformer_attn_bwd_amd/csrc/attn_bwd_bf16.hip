@@ -205,6 +205,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // 1 during the first C ops.
         constexpr int SM0 = NAT + 2;
         constexpr int SM1 = NA + 1;
+        static_assert(SM0 + 4 < NA, "half 0 softmax must finish before the C ops");
+        static_assert(SM1 + 4 < NA + NCT, "half 1 softmax must finish before its C ops");
 
         bf16x8 fr[PD];
         static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
@@ -271,25 +273,18 @@ template <int D, int DV>
 struct DqCfg {
     static constexpr int BM = 128;           // queries per workgroup, 32 per wave
     static constexpr int BN = 64;            // keys per step
-    static constexpr int LDK = D + 8;
-    static constexpr int LDV = DV + 8;
-    static constexpr int LDT = BN + 4;
-    static constexpr int K_ITEMS = (BN / 4) * (D / 8);   // 4 rows x 8 columns each
-    static constexpr int V_ITEMS = BN * DV / 8;          // 16-byte chunks
-    static constexpr int K_PER_T = (K_ITEMS + 255) / 256;
-    static constexpr int V_PER_T = (V_ITEMS + 255) / 256;
 };
 
 template <int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ Dw, bf16* __restrict__ dq, int n, int m, int n_pad, float scale,
     float c2) {
     using C = DqCfg<D, DV>;
-    __shared__ __align__(16) bf16 sK[2][C::BN * C::LDK];
-    __shared__ __align__(16) bf16 sKT[2][D * C::LDT];
-    __shared__ __align__(16) bf16 sV[2][C::BN * C::LDV];
+    constexpr int BN = C::BN;
+    __shared__ __align__(1024) bf16 sK[2][BN * D];
+    __shared__ __align__(1024) bf16 sV[2][BN * DV];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -315,128 +310,120 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const float Dq = Dw[bh * (long)n_pad + myq];
 
     const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
-    const int nsteps = (k_end + C::BN - 1) / C::BN;
+    const int nsteps = (k_end + BN - 1) / BN;
 
-    u32x4 kst[C::K_PER_T][4], vst[C::V_PER_T];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int it = 0; it < C::K_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::K_ITEMS) {
-                const int rg = e / (D / 8), cg = e % (D / 8);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int key = k0 + 4 * rg + x;
-                    kst[it][x] = key < m ? gload16(kh + (long)key * D + 8 * cg) : u32x4{0, 0, 0, 0};
-                }
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::V_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::V_ITEMS) {
-                const int r = e / (DV / 8), cg = e % (DV / 8);
-                const int key = k0 + r;
-                vst[it] = key < m ? gload16(vh + (long)key * DV + 8 * cg) : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto commit = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < C::K_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::K_ITEMS) {
-                const int rg = e / (D / 8), cg = e % (D / 8);
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    lds_write16(&sK[buf][(4 * rg + x) * C::LDK + 8 * cg], kst[it][x]);
-#pragma unroll
-                for (int y = 0; y < 8; ++y)
-                    lds_write8(&sKT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(kst[it], y));
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::V_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::V_ITEMS) {
-                const int r = e / (DV / 8), cg = e % (DV / 8);
-                lds_write16(&sV[buf][r * C::LDV + 8 * cg], vst[it]);
-            }
-        }
+    // Key rows past m repeat row m-1; they are masked below.
+    auto stage = [&](int buf, int k0) {
+        tile_load_async<D, BN>(sK[buf], kh, k0, m, wave, 4, lane);
+        tile_load_async<DV, BN>(sV[buf], vh, k0, m, wave, 4, lane);
     };
 
     f32x16 acc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = zero16();
 
-    if (nsteps > 0) {
-        fetch(0);
-        commit(0);
-    }
+    if (nsteps > 0) stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int step = 0; step < nsteps; ++step) {
         const int buf = step & 1;
-        const int k0 = step * C::BN;
-        const bool has_next = step + 1 < nsteps;
-        if (has_next) fetch(k0 + C::BN);
+        const int k0 = step * BN;
+        if (step + 1 < nsteps) stage(buf ^ 1, k0 + BN);
 
         const bf16* Ks = sK[buf];
         const bf16* Vs = sV[buf];
-        f32x16 S[2], dP[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            S[t] = zero16();
-            dP[t] = zero16();
-        }
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 a = lds_read8(Ks + (32 * t + li) * C::LDK + 16 * kc + 8 * g);
-                S[t] = mfma32(a, qreg[kc], S[t]);
-            }
-        }
-#pragma unroll
-        for (int kc = 0; kc < DV / 16; ++kc) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 a = lds_read8(Vs + (32 * t + li) * C::LDV + 16 * kc + 8 * g);
-                dP[t] = mfma32(a, oreg[kc], dP[t]);
-            }
-        }
+        const bool need_mask = (CAUSAL && k0 + BN - 1 > i0) || (k0 + BN > m);
 
-        const bool need_mask = (CAUSAL && k0 + C::BN - 1 > i0) || (k0 + C::BN > m);
+        // Products of the step, one per slot:
+        //   A ops (per 32-key half t): S^T[t] += K_t Q^T (D/16), dP^T[t] += V_t dO^T (DV/16)
+        //   C ops (per t, c):          dQ^T += K^T dS^T (D/32)
+        constexpr int KA = D / 16, KB = DV / 16;
+        constexpr int NAT = KA + KB, NA = 2 * NAT;
+        constexpr int NCT = 2 * (D / 32), NC = 2 * NCT;
+        constexpr int NOPS = NA + NC;
+        constexpr int PD = 4;
+
+        auto load_op = [&](auto oc_) -> bf16x8 {
+            constexpr int o = decltype(oc_)::value;
+            if constexpr (o < NA) {
+                constexpr int t = o / NAT, r = o % NAT;
+                if constexpr (r < KA) return tile_read8<D>(Ks, 32 * t + li, 2 * r + g);
+                else return tile_read8<DV>(Vs, 32 * t + li, 2 * (r - KA) + g);
+            } else {
+                constexpr int oc = o - NA;
+                constexpr int t = oc / NCT, rc = oc % NCT;
+                constexpr int c = rc / (D / 32), x = rc % (D / 32);
+                return tile_read_tr<D>(Ks, 32 * t + 16 * c, 32 * x, lane);
+            }
+        };
+
+        f32x16 S[2], dP[2];
         bf16x8 dSb[2][2];
+        float ds[16];
+        // dS^T of half T for accumulator slots 4VQ..4VQ+3 (keys of those slots).
+        auto softmax_part = [&](auto t_, auto vq_) {
+            constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            float ds[16];
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
+            for (int r = 0; r < 4; ++r) {
+                const int vv = 4 * vq + r;
+                const int key = k0 + 32 * t + 8 * vq + 4 * g + r;
                 float pv = fast_exp2(S[t][vv] * c2 - l2);
-                if (need_mask) {
-                    const int key = k0 + 32 * t + 8 * (vv >> 2) + 4 * g + (vv & 3);
-                    if (key >= m || (CAUSAL && key > myq)) pv = 0.f;
-                }
+                pv = (need_mask && (key >= m || (CAUSAL && key > myq))) ? 0.f : pv;
                 ds[vv] = pv * (dP[t][vv] - Dq);
             }
+        };
+        auto pack_half = [&](auto t_) {
+            constexpr int t = decltype(t_)::value;
             dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
             dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-        }
+        };
+        constexpr int SM0 = NAT + 2;
+        constexpr int SM1 = NA + 1;
+        constexpr int PPS1 = NCT >= 6 ? 1 : 2;
+        static_assert(SM0 + 4 < NA, "half 0 softmax must finish before the C ops");
+        static_assert(SM1 + 4 / PPS1 < NA + NCT, "half 1 softmax must finish before its C ops");
 
-        // dQ^T (d x queries) += K^T dS^T: A = K^T from sKT, B = dS^T from registers.
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) {
-            const bf16* row = sKT[buf] + (32 * mt + li) * C::LDT;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    acc[mt] = mfma32(read_rowc_pair(row, 32 * t + 16 * c, g), dSb[t][c], acc[mt]);
+        bf16x8 fr[PD];
+        static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
+        __builtin_amdgcn_sched_barrier(0);
+
+        static_for<NOPS>([&](auto o_) {
+            constexpr int o = decltype(o_)::value;
+            const bf16x8 cur = fr[o % PD];
+            if constexpr (o + PD < NOPS)
+                fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
+            if constexpr (o < NA) {
+                constexpr int t = o / NAT, r = o % NAT;
+                if constexpr (r == 0) {
+                    S[t] = zero16();
+                    dP[t] = zero16();
+                }
+                if constexpr (r < KA) S[t] = mfma32(cur, qreg[r], S[t]);
+                else dP[t] = mfma32(cur, oreg[r - KA], dP[t]);
+            } else {
+                constexpr int oc = o - NA;
+                constexpr int t = oc / NCT, rc = oc % NCT;
+                constexpr int c = rc / (D / 32), x = rc % (D / 32);
+                acc[x] = mfma32(cur, dSb[t][c], acc[x]);
             }
-        }
+            if constexpr (o >= SM0 && o < SM0 + 4)
+                softmax_part(std::integral_constant<int, 0>{}, std::integral_constant<int, o - SM0>{});
+            if constexpr (o == SM0 + 4) pack_half(std::integral_constant<int, 0>{});
+            // Half 1 must be ready before the C ops that use it (the second
+            // half of the C ops), so it runs over the first ones, two row
+            // groups per slot when there are few of them.
+            if constexpr (o >= SM1 && o < SM1 + 4 / PPS1) {
+                static_for<PPS1>([&](auto j_) {
+                    constexpr int vq = (o - SM1) * PPS1 + decltype(j_)::value;
+                    softmax_part(std::integral_constant<int, 1>{}, std::integral_constant<int, vq>{});
+                });
+            }
+            if constexpr (o == SM1 + 4 / PPS1) pack_half(std::integral_constant<int, 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
 
-        if (has_next) commit(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
