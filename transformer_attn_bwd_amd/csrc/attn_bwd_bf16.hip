@@ -99,16 +99,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int kc = 0; kc < DV / 16; ++kc)
         vreg[kc] = myk < m ? gload_bf16x8(vh + (long)myk * DV + 16 * kc + 8 * g) : bf16x8{};
 
+    TileOffsets<D> toQ;
+    toQ.init(lane);
+    TileOffsets<DV> toO;
+    toO.init(lane);
+
     const int i_begin = CAUSAL ? (j0 / BM) * BM : 0;
     const int i_end = (n + BM - 1) / BM * BM;
     const int nsteps = (i_end - i_begin) / BM;
 
-    // Stage query tile i0 into buffer buf: Q and dO rows (rows past n repeat
+    // Stage query tile i0 into buffer BUF: Q and dO rows (rows past n repeat
     // row n-1; their LSE2 is +inf, so P = 0 and they contribute nothing),
     // and the per-row LSE2 and D.
-    auto stage = [&](int buf, int i0) {
-        tile_load_async<D, BM>(sQ[buf], qh, i0, n, wave, 4, lane);
-        tile_load_async<DV, BM>(sO[buf], oh, i0, n, wave, 4, lane);
+    auto stage = [&](auto buf_, int i0) {
+        constexpr int buf = decltype(buf_)::value;
+        tile_load_split<D, BM, 4>(sQ[buf], qh, i0, n, wave, lane);
+        tile_load_split<DV, BM, 4>(sO[buf], oh, i0, n, wave, lane);
         if (wave == 0)
             __builtin_amdgcn_global_load_lds(lh + i0 + lane, (ATTN_LDS void*)sL[buf], 4, 0, 0);
         else if (wave == 1)
@@ -121,33 +127,27 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int t = 0; t < DV / 32; ++t) accV[t] = zero16();
 
-    if (nsteps > 0) stage(0, i_begin);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int step = 0; step < nsteps; ++step) {
-        const int buf = step & 1;
-        const int i0 = i_begin + step * BM;
-        if (step + 1 < nsteps) stage(buf ^ 1, i0 + BM);
-
+    // One query tile.  The step is a fixed sequence of NA + NC products,
+    // issued one per slot in this order:
+    //   A ops (per query half t): S[t] += Q_t K^T (D/16), dP[t] += dO_t V^T (DV/16)
+    //   C ops (per t, c):         dV += P^T dO (DV/32), dK += dS^T Q (D/32)
+    // Each product's LDS operand is fetched PD slots ahead, and the softmax
+    // of one half is spread over the slots of the other half's products, so
+    // that the matrix cores, the LDS and the vector ALUs work at the same
+    // time.  Slots are fenced with sched_barrier so the compiler keeps this
+    // order.  MASKED steps apply the causal mask (tiles on the diagonal).
+    auto compute = [&](auto buf_, auto masked_, int i0) {
+        constexpr int buf = decltype(buf_)::value;
+        constexpr bool MASKED = decltype(masked_)::value;
         const bf16* Qs = sQ[buf];
         const bf16* Os = sO[buf];
         const float* Ls = sL[buf];
         const float* Dsm = sD[buf];
-        const bool need_mask = CAUSAL && (i0 < j0 + C::BN - 1);
 
-        // The step is a fixed sequence of NA + NC products, issued one per
-        // slot in this order:
-        //   A ops (per query half t): S[t] += Q_t K^T (D/16), dP[t] += dO_t V^T (DV/16)
-        //   C ops (per t, c):         dV += P^T dO (DV/32), dK += dS^T Q (D/32)
-        // Each product's LDS operand is fetched PD slots ahead, and the
-        // softmax of one half is spread over the slots of the other half's
-        // products, so that the matrix cores, the LDS and the vector ALUs
-        // work at the same time.  Slots are fenced with sched_barrier so the
-        // compiler keeps this order.
         constexpr int KA = D / 16, KB = DV / 16;
         constexpr int NAT = KA + KB, NA = 2 * NAT;
-        constexpr int NCT = 2 * (DV / 32 + D / 32), NC = 2 * NCT;
+        constexpr int NCX = DV / 32 + D / 32;
+        constexpr int NCT = 2 * NCX, NC = 2 * NCT;
         constexpr int NOPS = NA + NC;
         constexpr int PD = 4;
 
@@ -155,14 +155,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             constexpr int o = decltype(oc_)::value;
             if constexpr (o < NA) {
                 constexpr int t = o / NAT, r = o % NAT;
-                if constexpr (r < KA) return tile_read8<D>(Qs, 32 * t + li, 2 * r + g);
-                else return tile_read8<DV>(Os, 32 * t + li, 2 * (r - KA) + g);
+                if constexpr (r < KA) return tile_read8_at<D>(Qs, toQ, 32 * t, r);
+                else return tile_read8_at<DV>(Os, toO, 32 * t, r - KA);
             } else {
                 constexpr int oc = o - NA;
                 constexpr int t = oc / NCT, rc = oc % NCT;
-                constexpr int c = rc / (DV / 32 + D / 32), x = rc % (DV / 32 + D / 32);
-                if constexpr (x < DV / 32) return tile_read_tr<DV>(Os, 32 * t + 16 * c, 32 * x, lane);
-                else return tile_read_tr<D>(Qs, 32 * t + 16 * c, 32 * (x - DV / 32), lane);
+                constexpr int c = rc / NCX, x = rc % NCX;
+                if constexpr (x < DV / 32) return tile_read_tr_at<DV>(Os, toO, 32 * t + 16 * c, x);
+                else return tile_read_tr_at<D>(Qs, toQ, 32 * t + 16 * c, x - DV / 32);
             }
         };
 
@@ -171,23 +171,25 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         f32x4 l4[4], d4[4];
         float p[16], ds[16];
 
-        auto load_stats = [&](int t) {
-#pragma unroll
-            for (int vq = 0; vq < 4; ++vq) {
-                const int qoff = 32 * t + 8 * vq + 4 * g;
-                l4[vq] = *reinterpret_cast<const f32x4*>(Ls + qoff);
-                d4[vq] = *reinterpret_cast<const f32x4*>(Dsm + qoff);
-            }
+        auto load_stats = [&](auto t_, auto vq_) {
+            constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
+            l4[vq] = *reinterpret_cast<const f32x4*>(Ls + 32 * t + 8 * vq + 4 * g);
+            d4[vq] = *reinterpret_cast<const f32x4*>(Dsm + 32 * t + 8 * vq + 4 * g);
         };
-        // Softmax of half T, rows 4VQ..4VQ+3 of the accumulator slots.
+        // Softmax of half T for accumulator slots 4VQ..4VQ+3:
+        // P = exp2(S*scale*log2e - LSE2), dS = P (dP - D).
         auto softmax_part = [&](auto t_, auto vq_) {
             constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
-            const int qoff = 32 * t + 8 * vq + 4 * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
+                constexpr int dummy = 0;
+                (void)dummy;
                 const int vv = 4 * vq + r;
-                float pv = fast_exp2(S[t][vv] * c2 - l4[vq][r]);
-                pv = (need_mask && myk > i0 + qoff + r) ? 0.f : pv;
+                float pv = fast_exp2(__builtin_fmaf(S[t][vv], c2, -l4[vq][r]));
+                if constexpr (MASKED) {
+                    const int qrow = i0 + 32 * t + 8 * vq + 4 * g + r;
+                    pv = myk > qrow ? 0.f : pv;
+                }
                 p[vv] = pv;
                 ds[vv] = pv * (dP[t][vv] - d4[vq][r]);
             }
@@ -200,9 +202,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
         };
 
-        // Slots at which the softmax pieces of each half run: half 0 during
-        // the A ops of half 1 (after its inputs have had time to land), half
-        // 1 during the first C ops.
+        // Slots of the softmax pieces: half 0 during the A ops of half 1
+        // (after its inputs have had time to land), half 1 during the first
+        // C ops.  Row statistics are read one slot before each piece.
         constexpr int SM0 = NAT + 2;
         constexpr int SM1 = NA + 1;
         static_assert(SM0 + 4 < NA, "half 0 softmax must finish before the C ops");
@@ -210,11 +212,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
         bf16x8 fr[PD];
         static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
-        load_stats(0);
         __builtin_amdgcn_sched_barrier(0);
 
         static_for<NOPS>([&](auto o_) {
             constexpr int o = decltype(o_)::value;
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
             const bf16x8 cur = fr[o % PD];
             if constexpr (o + PD < NOPS)
                 fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
@@ -229,25 +232,55 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             } else {
                 constexpr int oc = o - NA;
                 constexpr int t = oc / NCT, rc = oc % NCT;
-                constexpr int c = rc / (DV / 32 + D / 32), x = rc % (DV / 32 + D / 32);
+                constexpr int c = rc / NCX, x = rc % NCX;
                 if constexpr (x < DV / 32) accV[x] = mfma32(Pb[t][c], cur, accV[x]);
                 else accK[x - DV / 32] = mfma32(dSb[t][c], cur, accK[x - DV / 32]);
             }
+            if constexpr (o >= SM0 - 1 && o < SM0 + 3)
+                load_stats(I0{}, std::integral_constant<int, o - SM0 + 1>{});
             if constexpr (o >= SM0 && o < SM0 + 4)
-                softmax_part(std::integral_constant<int, 0>{}, std::integral_constant<int, o - SM0>{});
-            if constexpr (o == SM0 + 4) {
-                pack_half(std::integral_constant<int, 0>{});
-                load_stats(1);
-            }
+                softmax_part(I0{}, std::integral_constant<int, o - SM0>{});
+            if constexpr (o == SM0 + 4) pack_half(I0{});
+            if constexpr (o >= SM1 - 1 && o < SM1 + 3)
+                load_stats(I1{}, std::integral_constant<int, o - SM1 + 1>{});
             if constexpr (o >= SM1 && o < SM1 + 4)
-                softmax_part(std::integral_constant<int, 1>{}, std::integral_constant<int, o - SM1>{});
-            if constexpr (o == SM1 + 4) pack_half(std::integral_constant<int, 1>{});
+                softmax_part(I1{}, std::integral_constant<int, o - SM1>{});
+            if constexpr (o == SM1 + 4) pack_half(I1{});
             __builtin_amdgcn_sched_barrier(0);
         });
+    };
 
+    auto do_step = [&](auto buf_, auto masked_, int s) {
+        constexpr int buf = decltype(buf_)::value;
+        const int i0 = i_begin + s * BM;
+        if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, i0 + BM);
+        compute(buf_, masked_, i0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using MaskOn = std::integral_constant<bool, true>;
+    using MaskOff = std::integral_constant<bool, false>;
+
+    if (nsteps > 0) stage(B0{}, i_begin);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    int s = 0;
+    if constexpr (CAUSAL) {
+        // Query tiles that overlap keys j0..j0+BN-1 straddle the diagonal;
+        // with BN = 2 BM these are the first two, buffers 0 and 1.
+        static_assert(C::BN == 2 * BM, "two masked steps per key block");
+        if (s < nsteps) do_step(B0{}, MaskOn{}, s++);
+        if (s < nsteps) do_step(B1{}, MaskOn{}, s++);
     }
+    for (; s + 1 < nsteps; s += 2) {
+        do_step(B0{}, MaskOff{}, s);
+        do_step(B1{}, MaskOff{}, s + 1);
+    }
+    if (s < nsteps) do_step(B0{}, MaskOff{}, s);
 
     // Accumulator slot vv of tile nt holds key kw0 + 8*(vv>>2) + 4g + (vv&3),
     // column 32*nt + li.
@@ -309,35 +342,40 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const float l2 = lse2[bh * (long)n_pad + myq];
     const float Dq = Dw[bh * (long)n_pad + myq];
 
+    TileOffsets<D> toK;
+    toK.init(lane);
+    TileOffsets<DV> toV;
+    toV.init(lane);
+
     const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
     const int nsteps = (k_end + BN - 1) / BN;
+    // Leading steps that need no mask: entirely below the diagonal and
+    // entirely inside the m keys.  The rest (at the end) are masked.
+    int n_plain = min(nsteps, m / BN);
+    if (CAUSAL) n_plain = min(n_plain, i0 / BN);
 
-    // Key rows past m repeat row m-1; they are masked below.
-    auto stage = [&](int buf, int k0) {
-        tile_load_async<D, BN>(sK[buf], kh, k0, m, wave, 4, lane);
-        tile_load_async<DV, BN>(sV[buf], vh, k0, m, wave, 4, lane);
+    // Key rows past m repeat row m-1; masked steps zero their P.
+    auto stage = [&](auto buf_, int k0) {
+        constexpr int buf = decltype(buf_)::value;
+        tile_load_split<D, BN, 4>(sK[buf], kh, k0, m, wave, lane);
+        tile_load_split<DV, BN, 4>(sV[buf], vh, k0, m, wave, lane);
     };
 
     f32x16 acc[D / 32];
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = zero16();
 
-    if (nsteps > 0) stage(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int step = 0; step < nsteps; ++step) {
-        const int buf = step & 1;
-        const int k0 = step * BN;
-        if (step + 1 < nsteps) stage(buf ^ 1, k0 + BN);
-
+    // One key tile: products one per slot,
+    //   A ops (per 32-key half t): S^T[t] += K_t Q^T (D/16), dP^T[t] += V_t dO^T (DV/16)
+    //   C ops (per t, c):          dQ^T += K^T dS^T (D/32)
+    // with operand reads PD slots ahead and the softmax of one half spread
+    // over the other half's products (see the dK/dV kernel).
+    auto compute = [&](auto buf_, auto masked_, int k0) {
+        constexpr int buf = decltype(buf_)::value;
+        constexpr bool MASKED = decltype(masked_)::value;
         const bf16* Ks = sK[buf];
         const bf16* Vs = sV[buf];
-        const bool need_mask = (CAUSAL && k0 + BN - 1 > i0) || (k0 + BN > m);
 
-        // Products of the step, one per slot:
-        //   A ops (per 32-key half t): S^T[t] += K_t Q^T (D/16), dP^T[t] += V_t dO^T (DV/16)
-        //   C ops (per t, c):          dQ^T += K^T dS^T (D/32)
         constexpr int KA = D / 16, KB = DV / 16;
         constexpr int NAT = KA + KB, NA = 2 * NAT;
         constexpr int NCT = 2 * (D / 32), NC = 2 * NCT;
@@ -348,28 +386,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             constexpr int o = decltype(oc_)::value;
             if constexpr (o < NA) {
                 constexpr int t = o / NAT, r = o % NAT;
-                if constexpr (r < KA) return tile_read8<D>(Ks, 32 * t + li, 2 * r + g);
-                else return tile_read8<DV>(Vs, 32 * t + li, 2 * (r - KA) + g);
+                if constexpr (r < KA) return tile_read8_at<D>(Ks, toK, 32 * t, r);
+                else return tile_read8_at<DV>(Vs, toV, 32 * t, r - KA);
             } else {
                 constexpr int oc = o - NA;
                 constexpr int t = oc / NCT, rc = oc % NCT;
                 constexpr int c = rc / (D / 32), x = rc % (D / 32);
-                return tile_read_tr<D>(Ks, 32 * t + 16 * c, 32 * x, lane);
+                return tile_read_tr_at<D>(Ks, toK, 32 * t + 16 * c, x);
             }
         };
 
         f32x16 S[2], dP[2];
         bf16x8 dSb[2][2];
         float ds[16];
-        // dS^T of half T for accumulator slots 4VQ..4VQ+3 (keys of those slots).
         auto softmax_part = [&](auto t_, auto vq_) {
             constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int vv = 4 * vq + r;
-                const int key = k0 + 32 * t + 8 * vq + 4 * g + r;
-                float pv = fast_exp2(S[t][vv] * c2 - l2);
-                pv = (need_mask && (key >= m || (CAUSAL && key > myq))) ? 0.f : pv;
+                float pv = fast_exp2(__builtin_fmaf(S[t][vv], c2, -l2));
+                if constexpr (MASKED) {
+                    const int key = k0 + 32 * t + 8 * vq + 4 * g + r;
+                    pv = (key >= m || (CAUSAL && key > myq)) ? 0.f : pv;
+                }
                 ds[vv] = pv * (dP[t][vv] - Dq);
             }
         };
@@ -390,6 +429,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
         static_for<NOPS>([&](auto o_) {
             constexpr int o = decltype(o_)::value;
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
             const bf16x8 cur = fr[o % PD];
             if constexpr (o + PD < NOPS)
                 fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
@@ -408,23 +449,48 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 acc[x] = mfma32(cur, dSb[t][c], acc[x]);
             }
             if constexpr (o >= SM0 && o < SM0 + 4)
-                softmax_part(std::integral_constant<int, 0>{}, std::integral_constant<int, o - SM0>{});
-            if constexpr (o == SM0 + 4) pack_half(std::integral_constant<int, 0>{});
-            // Half 1 must be ready before the C ops that use it (the second
-            // half of the C ops), so it runs over the first ones, two row
-            // groups per slot when there are few of them.
+                softmax_part(I0{}, std::integral_constant<int, o - SM0>{});
+            if constexpr (o == SM0 + 4) pack_half(I0{});
+            // Half 1 runs over the first C ops, two row groups per slot when
+            // there are few of them.
             if constexpr (o >= SM1 && o < SM1 + 4 / PPS1) {
                 static_for<PPS1>([&](auto j_) {
                     constexpr int vq = (o - SM1) * PPS1 + decltype(j_)::value;
-                    softmax_part(std::integral_constant<int, 1>{}, std::integral_constant<int, vq>{});
+                    softmax_part(I1{}, std::integral_constant<int, vq>{});
                 });
             }
-            if constexpr (o == SM1 + 4 / PPS1) pack_half(std::integral_constant<int, 1>{});
+            if constexpr (o == SM1 + 4 / PPS1) pack_half(I1{});
             __builtin_amdgcn_sched_barrier(0);
         });
+    };
 
+    auto do_step = [&](auto buf_, auto masked_, int s) {
+        constexpr int buf = decltype(buf_)::value;
+        const int k0 = s * BN;
+        if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, k0 + BN);
+        compute(buf_, masked_, k0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using MaskOn = std::integral_constant<bool, true>;
+    using MaskOff = std::integral_constant<bool, false>;
+
+    if (nsteps > 0) stage(B0{}, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    int s = 0;
+    for (; s + 1 < n_plain; s += 2) {
+        do_step(B0{}, MaskOff{}, s);
+        do_step(B1{}, MaskOff{}, s + 1);
+    }
+    if (s < n_plain) do_step(B0{}, MaskOff{}, s++);
+    for (; s < nsteps; ++s) {
+        if (s & 1) do_step(B1{}, MaskOn{}, s);
+        else do_step(B0{}, MaskOn{}, s);
     }
 
     // Accumulator slot vv of tile mt holds column d = 32*mt + 8*(vv>>2) + 4g + (vv&3)

@@ -148,6 +148,81 @@ struct SwzTile {
     __device__ static __forceinline__ int off(int r, int c) { return r * C + 8 * (c ^ swz(r)); }
 };
 
+// Per-lane element offsets into a swizzled C-wide tile for the two read
+// patterns the kernels use.  Row-block parts that are multiples of 16 rows
+// (query or key halves, 16-row halves of a C tile) do not change the
+// swizzle, so they are left to the instructions' immediate offsets.
+//  a[kc]:      operand read of row (lane & 31), chunk 2*kc + (lane >> 5)
+//  tr[h][nt]:  transposing read of rows 4g + (j>>2) + 8h (g = lane>>5,
+//              j = lane & 15), columns 32*nt + 16*((lane>>4)&1) + 4*(j&3)
+template <int C>
+struct TileOffsets {
+    int a[C / 16];
+    int tr[2][C / 32];
+    __device__ __forceinline__ void init(int lane) {
+        using T = SwzTile<C>;
+        const int li = lane & 31, g = lane >> 5;
+#pragma unroll
+        for (int kc = 0; kc < C / 16; ++kc) a[kc] = T::off(li, 2 * kc + g);
+        const int blk = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 4 * g + (j >> 2) + 8 * h;
+#pragma unroll
+            for (int nt = 0; nt < C / 32; ++nt) {
+                const int col = 32 * nt + 16 * (blk & 1) + 4 * (j & 3);
+                tr[h][nt] = T::off(r, col >> 3) + (col & 7);
+            }
+        }
+    }
+};
+
+// Operand read through precomputed offsets: rows row0 + (lane & 31) of a
+// tile at `tile` (row0 a multiple of 16), chunk 2*kc + g.
+template <int C>
+__device__ __forceinline__ bf16x8 tile_read8_at(const bf16* tile, const TileOffsets<C>& to,
+                                                int row0, int kc) {
+    return *reinterpret_cast<const bf16x8*>(tile + row0 * C + to.a[kc]);
+}
+
+// Transposing read through precomputed offsets; `base` (a multiple of 16)
+// is the first of the 16 tile rows that form the k range, nt the 32-column
+// block: lane l gets column 32*nt + (l & 31) of rows base+4g..+3 and
+// base+8+4g..+3.
+template <int C>
+__device__ __forceinline__ bf16x8 tile_read_tr_at(const bf16* tile, const TileOffsets<C>& to,
+                                                  int base, int nt) {
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (ATTN_LDS i16x4*)(tile + base * C + to.tr[0][nt]));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (ATTN_LDS i16x4*)(tile + base * C + to.tr[1][nt]));
+    i16x4 both[2] = {lo, hi};
+    return *reinterpret_cast<bf16x8*>(both);
+}
+
+// Fill ROWS rows of a swizzled tile from global rows row0.. of a [*, C]
+// row-major bf16 matrix, the work split over NW waves (this is wave w);
+// rows at or past `valid` read row valid-1 instead (callers neutralise
+// them).
+template <int C, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_split(bf16* lds_tile, const bf16* g, int row0,
+                                                int valid, int w, int lane) {
+    using T = SwzTile<C>;
+    constexpr int INSTS = ROWS * T::CPR / 64;
+    static_assert(INSTS % NW == 0, "tile loads must split evenly over the waves");
+#pragma unroll
+    for (int jj = 0; jj < INSTS / NW; ++jj) {
+        const int ii = w + NW * jj;
+        const int p = ii * 64 + lane;
+        const int r = p / T::CPR;
+        const int s = p % T::CPR;
+        int grow = row0 + r;
+        grow = grow < valid ? grow : valid - 1;
+        const bf16* src = g + (long)grow * C + 8 * (s ^ T::swz(r));
+        __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + ii * 512), 16, 0, 0);
+    }
+}
+
 // Fill `rows` rows of a swizzled tile from global rows row0.. of a [*, C]
 // row-major bf16 matrix; rows at or past `valid` read row valid-1 instead
 // (callers neutralise them).  Called by `nw` waves, wave `w`.
