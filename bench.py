@@ -61,7 +61,9 @@ def bwd_bytes(w) -> float:
     return float(qk + vo + grads + rows)
 
 
-def time_loop(fn, steps, torch):
+def time_loop(fn, steps, torch, warmup=0):
+    for _ in range(warmup):
+        fn()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -99,8 +101,8 @@ def cpu_baseline(w, inputs, heads_wanted):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0)
@@ -162,11 +164,11 @@ def main():
 
     # per-kernel average launch durations (HIP events on the launch stream)
     kern_ms = {
-        "preprocess": time_loop(lambda: bwd_step(["preprocess"]), args.steps, torch),
-        "dkdv": time_loop(lambda: bwd_step(["dkdv"]), args.steps, torch),
-        "dq": time_loop(lambda: bwd_step(["dq"]), args.steps, torch),
+        "preprocess": time_loop(lambda: bwd_step(["preprocess"]), args.steps, torch, 3),
+        "dkdv": time_loop(lambda: bwd_step(["dkdv"]), args.steps, torch, 3),
+        "dq": time_loop(lambda: bwd_step(["dq"]), args.steps, torch, 3),
     }
-    fwd_ms = time_loop(fwd_step, args.steps, torch)
+    fwd_ms = time_loop(fwd_step, args.steps, torch, 3)
     # restore outputs of a whole backward after the single-stage runs
     bwd_step()
     torch.cuda.synchronize()

@@ -25,6 +25,16 @@
 namespace attn {
 namespace {
 
+// Order of the S and dP products within a query (or key) half: the two
+// accumulation chains alternate so that consecutive products never depend
+// on each other; the longer chain's remainder goes last.
+template <int KA, int KB>
+constexpr int a_order(int r0) {
+    constexpr int m = KA < KB ? KA : KB;
+    if (r0 < 2 * m) return (r0 & 1) ? KA + r0 / 2 : r0 / 2;
+    return KA > KB ? (r0 - m) : (KA + (r0 - m));
+}
+
 // ---------------------------------------------------------------- preprocess
 
 template <int DV>
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Stage query tile i0 into buffer BUF: Q and dO rows (rows past n repeat
     // row n-1; their LSE2 is +inf, so P = 0 and they contribute nothing),
     // and the per-row LSE2 and D.
-    auto stage = [&](auto buf_, int i0) {
+    auto stage = [&](auto buf_, int i0) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_)::value;
         tile_load_split<D, BM, 4>(sQ[buf], qh, i0, n, wave, lane);
         tile_load_split<DV, BM, 4>(sO[buf], oh, i0, n, wave, lane);
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // that the matrix cores, the LDS and the vector ALUs work at the same
     // time.  Slots are fenced with sched_barrier so the compiler keeps this
     // order.  MASKED steps apply the causal mask (tiles on the diagonal).
-    auto compute = [&](auto buf_, auto masked_, int i0) {
+    auto compute = [&](auto buf_, auto masked_, int i0) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_)::value;
         constexpr bool MASKED = decltype(masked_)::value;
         const bf16* Qs = sQ[buf];
@@ -151,10 +161,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr int NOPS = NA + NC;
         constexpr int PD = 4;
 
-        auto load_op = [&](auto oc_) -> bf16x8 {
+        auto load_op = [&](auto oc_) __attribute__((always_inline)) -> bf16x8 {
             constexpr int o = decltype(oc_)::value;
             if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = o % NAT;
+                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
                 if constexpr (r < KA) return tile_read8_at<D>(Qs, toQ, 32 * t, r);
                 else return tile_read8_at<DV>(Os, toO, 32 * t, r - KA);
             } else {
@@ -171,14 +181,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         f32x4 l4[4], d4[4];
         float p[16], ds[16];
 
-        auto load_stats = [&](auto t_, auto vq_) {
+        auto load_stats = [&](auto t_, auto vq_) __attribute__((always_inline)) {
             constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
             l4[vq] = *reinterpret_cast<const f32x4*>(Ls + 32 * t + 8 * vq + 4 * g);
             d4[vq] = *reinterpret_cast<const f32x4*>(Dsm + 32 * t + 8 * vq + 4 * g);
         };
         // Softmax of half T for accumulator slots 4VQ..4VQ+3:
         // P = exp2(S*scale*log2e - LSE2), dS = P (dP - D).
-        auto softmax_part = [&](auto t_, auto vq_) {
+        auto softmax_part = [&](auto t_, auto vq_) __attribute__((always_inline)) {
             constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 ds[vv] = pv * (dP[t][vv] - d4[vq][r]);
             }
         };
-        auto pack_half = [&](auto t_) {
+        auto pack_half = [&](auto t_) __attribute__((always_inline)) {
             constexpr int t = decltype(t_)::value;
             Pb[t][0] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
             Pb[t][1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
@@ -222,8 +232,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             if constexpr (o + PD < NOPS)
                 fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
             if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = o % NAT;
-                if constexpr (r == 0) {
+                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
+                if constexpr (o % NAT == 0) {
                     S[t] = zero16();
                     dP[t] = zero16();
                 }
@@ -236,6 +246,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if constexpr (x < DV / 32) accV[x] = mfma32(Pb[t][c], cur, accV[x]);
                 else accK[x - DV / 32] = mfma32(dSb[t][c], cur, accK[x - DV / 32]);
             }
+
             if constexpr (o >= SM0 - 1 && o < SM0 + 3)
                 load_stats(I0{}, std::integral_constant<int, o - SM0 + 1>{});
             if constexpr (o >= SM0 && o < SM0 + 4)
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         });
     };
 
-    auto do_step = [&](auto buf_, auto masked_, int s) {
+    auto do_step = [&](auto buf_, auto masked_, int s) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_)::value;
         const int i0 = i_begin + s * BM;
         if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, i0 + BM);
@@ -355,7 +366,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if (CAUSAL) n_plain = min(n_plain, i0 / BN);
 
     // Key rows past m repeat row m-1; masked steps zero their P.
-    auto stage = [&](auto buf_, int k0) {
+    auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_)::value;
         tile_load_split<D, BN, 4>(sK[buf], kh, k0, m, wave, lane);
         tile_load_split<DV, BN, 4>(sV[buf], vh, k0, m, wave, lane);
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     //   C ops (per t, c):          dQ^T += K^T dS^T (D/32)
     // with operand reads PD slots ahead and the softmax of one half spread
     // over the other half's products (see the dK/dV kernel).
-    auto compute = [&](auto buf_, auto masked_, int k0) {
+    auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_)::value;
         constexpr bool MASKED = decltype(masked_)::value;
         const bf16* Ks = sK[buf];
@@ -382,10 +393,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr int NOPS = NA + NC;
         constexpr int PD = 4;
 
-        auto load_op = [&](auto oc_) -> bf16x8 {
+        auto load_op = [&](auto oc_) __attribute__((always_inline)) -> bf16x8 {
             constexpr int o = decltype(oc_)::value;
             if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = o % NAT;
+                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
                 if constexpr (r < KA) return tile_read8_at<D>(Ks, toK, 32 * t, r);
                 else return tile_read8_at<DV>(Vs, toV, 32 * t, r - KA);
             } else {
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         f32x16 S[2], dP[2];
         bf16x8 dSb[2][2];
         float ds[16];
-        auto softmax_part = [&](auto t_, auto vq_) {
+        auto softmax_part = [&](auto t_, auto vq_) __attribute__((always_inline)) {
             constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -412,7 +423,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 ds[vv] = pv * (dP[t][vv] - Dq);
             }
         };
-        auto pack_half = [&](auto t_) {
+        auto pack_half = [&](auto t_) __attribute__((always_inline)) {
             constexpr int t = decltype(t_)::value;
             dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
             dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
@@ -435,8 +446,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             if constexpr (o + PD < NOPS)
                 fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
             if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = o % NAT;
-                if constexpr (r == 0) {
+                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
+                if constexpr (o % NAT == 0) {
                     S[t] = zero16();
                     dP[t] = zero16();
                 }
@@ -448,6 +459,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 constexpr int c = rc / (D / 32), x = rc % (D / 32);
                 acc[x] = mfma32(cur, dSb[t][c], acc[x]);
             }
+
             if constexpr (o >= SM0 && o < SM0 + 4)
                 softmax_part(I0{}, std::integral_constant<int, o - SM0>{});
             if constexpr (o == SM0 + 4) pack_half(I0{});
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         });
     };
 
-    auto do_step = [&](auto buf_, auto masked_, int s) {
+    auto do_step = [&](auto buf_, auto masked_, int s) __attribute__((always_inline)) {
         constexpr int buf = decltype(buf_)::value;
         const int k0 = s * BN;
         if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, k0 + BN);

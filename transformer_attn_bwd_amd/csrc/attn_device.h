@@ -223,6 +223,24 @@ __device__ __forceinline__ void tile_load_split(bf16* lds_tile, const bf16* g, i
     }
 }
 
+// One of the INSTS/NW loads tile_load_split would issue (number jj), so
+// that a tile's loads can be spread over a step instead of issued at once.
+template <int C, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_one(bf16* lds_tile, const bf16* g, int row0, int valid,
+                                              int w, int lane, int jj) {
+    using T = SwzTile<C>;
+    const int ii = w + NW * jj;
+    const int p = ii * 64 + lane;
+    const int r = p / T::CPR;
+    const int s = p % T::CPR;
+    int grow = row0 + r;
+    grow = grow < valid ? grow : valid - 1;
+    const bf16* src = g + (long)grow * C + 8 * (s ^ T::swz(r));
+    __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + ii * 512), 16, 0, 0);
+}
+template <int C, int ROWS, int NW>
+constexpr int tile_loads_per_wave() { return ROWS * (C / 8) / 64 / NW; }
+
 // Fill `rows` rows of a swizzled tile from global rows row0.. of a [*, C]
 // row-major bf16 matrix; rows at or past `valid` read row valid-1 instead
 // (callers neutralise them).  Called by `nw` waves, wave `w`.
