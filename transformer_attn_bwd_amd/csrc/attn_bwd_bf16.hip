@@ -181,44 +181,40 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         f32x4 l4[4], d4[4];
         float p[16], ds[16];
 
+        // key > query  <=>  32t + 8vq + r < myk - i0 - 4g
+        const int mask_lim = myk - i0 - 4 * g;
         auto load_stats = [&](auto t_, auto vq_) __attribute__((always_inline)) {
             constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
             l4[vq] = *reinterpret_cast<const f32x4*>(Ls + 32 * t + 8 * vq + 4 * g);
             d4[vq] = *reinterpret_cast<const f32x4*>(Dsm + 32 * t + 8 * vq + 4 * g);
         };
-        // Softmax of half T for accumulator slots 4VQ..4VQ+3:
-        // P = exp2(S*scale*log2e - LSE2), dS = P (dP - D).
-        auto softmax_part = [&](auto t_, auto vq_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                constexpr int dummy = 0;
-                (void)dummy;
-                const int vv = 4 * vq + r;
-                float pv = fast_exp2(__builtin_fmaf(S[t][vv], c2, -l4[vq][r]));
-                if constexpr (MASKED) {
-                    const int qrow = i0 + 32 * t + 8 * vq + 4 * g + r;
-                    pv = myk > qrow ? 0.f : pv;
-                }
-                p[vv] = pv;
-                ds[vv] = pv * (dP[t][vv] - d4[vq][r]);
+        // One accumulator slot E of half T: P = exp2(S*scale*log2e - LSE2),
+        // dS = P (dP - D); after slots 7 and 15 the eight values are rounded
+        // to bf16 as one operand.
+        auto softmax_elem = [&](auto t_, auto e_) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_)::value, e = decltype(e_)::value;
+            constexpr int vq = e >> 2, r = e & 3;
+            float pv = fast_exp2(__builtin_fmaf(S[t][e], c2, -l4[vq][r]));
+            if constexpr (MASKED) pv = (32 * t + 8 * vq + r < mask_lim) ? 0.f : pv;
+            p[e] = pv;
+            ds[e] = pv * (dP[t][e] - d4[vq][r]);
+            if constexpr ((e & 7) == 7) {
+                constexpr int c = e >> 3, b = 8 * c;
+                Pb[t][c] = pack8(p[b], p[b + 1], p[b + 2], p[b + 3], p[b + 4], p[b + 5], p[b + 6], p[b + 7]);
+                dSb[t][c] = pack8(ds[b], ds[b + 1], ds[b + 2], ds[b + 3], ds[b + 4], ds[b + 5],
+                                  ds[b + 6], ds[b + 7]);
             }
         };
-        auto pack_half = [&](auto t_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value;
-            Pb[t][0] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            Pb[t][1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-            dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-            dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-        };
 
-        // Slots of the softmax pieces: half 0 during the A ops of half 1
-        // (after its inputs have had time to land), half 1 during the first
-        // C ops.  Row statistics are read one slot before each piece.
-        constexpr int SM0 = NAT + 2;
-        constexpr int SM1 = NA + 1;
-        static_assert(SM0 + 4 < NA, "half 0 softmax must finish before the C ops");
-        static_assert(SM1 + 4 < NA + NCT, "half 1 softmax must finish before its C ops");
+        // The softmax of each half is spread one or two accumulator slots per
+        // product over a window of slots, so that its exponentials and
+        // conversions overlap the matrix products instead of stalling them:
+        // half 0 over the A ops of half 1, half 1 over the C ops of half 0
+        // (finishing each bf16 operand before the first product that reads it).
+        constexpr int W0[2] = {NAT + 2, NA + 2};
+        constexpr int W1[2] = {NA, NA + NCT + NCX - 1};
+        static_assert(W1[0] > W0[0] && W1[1] > W0[1], "softmax windows");
+        static_assert(W0[1] + (7 * (W1[1] - W0[1])) / 16 < NA + NCT, "half 1 low operand in time");
 
         bf16x8 fr[PD];
         static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
@@ -226,8 +222,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
         static_for<NOPS>([&](auto o_) {
             constexpr int o = decltype(o_)::value;
-            using I0 = std::integral_constant<int, 0>;
-            using I1 = std::integral_constant<int, 1>;
             const bf16x8 cur = fr[o % PD];
             if constexpr (o + PD < NOPS)
                 fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
@@ -246,17 +240,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if constexpr (x < DV / 32) accV[x] = mfma32(Pb[t][c], cur, accV[x]);
                 else accK[x - DV / 32] = mfma32(dSb[t][c], cur, accK[x - DV / 32]);
             }
-
-            if constexpr (o >= SM0 - 1 && o < SM0 + 3)
-                load_stats(I0{}, std::integral_constant<int, o - SM0 + 1>{});
-            if constexpr (o >= SM0 && o < SM0 + 4)
-                softmax_part(I0{}, std::integral_constant<int, o - SM0>{});
-            if constexpr (o == SM0 + 4) pack_half(I0{});
-            if constexpr (o >= SM1 - 1 && o < SM1 + 3)
-                load_stats(I1{}, std::integral_constant<int, o - SM1 + 1>{});
-            if constexpr (o >= SM1 && o < SM1 + 4)
-                softmax_part(I1{}, std::integral_constant<int, o - SM1>{});
-            if constexpr (o == SM1 + 4) pack_half(I1{});
+            static_for<2>([&](auto t_) {
+                constexpr int t = decltype(t_)::value;
+                constexpr int L = W1[t] - W0[t];
+                // statistics for row group vq one slot before its first element
+                static_for<4>([&](auto vq_) {
+                    constexpr int vq = decltype(vq_)::value;
+                    if constexpr (W0[t] + (4 * vq * L) / 16 - 1 == o) load_stats(t_, vq_);
+                });
+                static_for<16>([&](auto e_) {
+                    constexpr int e = decltype(e_)::value;
+                    if constexpr (W0[t] + (e * L) / 16 == o) softmax_elem(t_, e_);
+                });
+            });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -410,29 +406,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         f32x16 S[2], dP[2];
         bf16x8 dSb[2][2];
         float ds[16];
-        auto softmax_part = [&](auto t_, auto vq_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int vv = 4 * vq + r;
-                float pv = fast_exp2(__builtin_fmaf(S[t][vv], c2, -l2));
-                if constexpr (MASKED) {
-                    const int key = k0 + 32 * t + 8 * vq + 4 * g + r;
-                    pv = (key >= m || (CAUSAL && key > myq)) ? 0.f : pv;
-                }
-                ds[vv] = pv * (dP[t][vv] - Dq);
+        // dS^T for accumulator slot E of half T (key k0 + 32T + 8(E>>2) + 4g
+        // + (E&3)); after slots 7 and 15 the eight values become one bf16
+        // operand.
+        auto softmax_elem = [&](auto t_, auto e_) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_)::value, e = decltype(e_)::value;
+            float pv = fast_exp2(__builtin_fmaf(S[t][e], c2, -l2));
+            if constexpr (MASKED) {
+                const int key = k0 + 32 * t + 8 * (e >> 2) + 4 * g + (e & 3);
+                pv = (key >= m || (CAUSAL && key > myq)) ? 0.f : pv;
+            }
+            ds[e] = pv * (dP[t][e] - Dq);
+            if constexpr ((e & 7) == 7) {
+                constexpr int c = e >> 3, b = 8 * c;
+                dSb[t][c] = pack8(ds[b], ds[b + 1], ds[b + 2], ds[b + 3], ds[b + 4], ds[b + 5],
+                                  ds[b + 6], ds[b + 7]);
             }
         };
-        auto pack_half = [&](auto t_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value;
-            dSb[t][0] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-            dSb[t][1] = pack8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-        };
-        constexpr int SM0 = NAT + 2;
-        constexpr int SM1 = NA + 1;
-        constexpr int PPS1 = NCT >= 6 ? 1 : 2;
-        static_assert(SM0 + 4 < NA, "half 0 softmax must finish before the C ops");
-        static_assert(SM1 + 4 / PPS1 < NA + NCT, "half 1 softmax must finish before its C ops");
+        // Softmax windows as in the dK/dV kernel: half 0 over the A ops of
+        // half 1, half 1 over the C ops of half 0.
+        constexpr int W0[2] = {NAT + 2, NA + 1};
+        constexpr int W1[2] = {NA, NA + NCT + (D / 32) - 1};
+        static_assert(W1[0] > W0[0] && W1[1] > W0[1], "softmax windows");
+        static_assert(W0[1] + (7 * (W1[1] - W0[1])) / 16 < NA + NCT, "half 1 low operand in time");
 
         bf16x8 fr[PD];
         static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
@@ -440,8 +436,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
         static_for<NOPS>([&](auto o_) {
             constexpr int o = decltype(o_)::value;
-            using I0 = std::integral_constant<int, 0>;
-            using I1 = std::integral_constant<int, 1>;
             const bf16x8 cur = fr[o % PD];
             if constexpr (o + PD < NOPS)
                 fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
@@ -459,19 +453,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 constexpr int c = rc / (D / 32), x = rc % (D / 32);
                 acc[x] = mfma32(cur, dSb[t][c], acc[x]);
             }
-
-            if constexpr (o >= SM0 && o < SM0 + 4)
-                softmax_part(I0{}, std::integral_constant<int, o - SM0>{});
-            if constexpr (o == SM0 + 4) pack_half(I0{});
-            // Half 1 runs over the first C ops, two row groups per slot when
-            // there are few of them.
-            if constexpr (o >= SM1 && o < SM1 + 4 / PPS1) {
-                static_for<PPS1>([&](auto j_) {
-                    constexpr int vq = (o - SM1) * PPS1 + decltype(j_)::value;
-                    softmax_part(I1{}, std::integral_constant<int, vq>{});
+            static_for<2>([&](auto t_) {
+                constexpr int t = decltype(t_)::value;
+                constexpr int L = W1[t] - W0[t];
+                static_for<16>([&](auto e_) {
+                    constexpr int e = decltype(e_)::value;
+                    if constexpr (W0[t] + (e * L) / 16 == o) softmax_elem(t_, e_);
                 });
-            }
-            if constexpr (o == SM1 + 4 / PPS1) pack_half(I1{});
+            });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
