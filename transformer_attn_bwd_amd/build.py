@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_f32.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip",
+           "attn_f32.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -51,7 +52,7 @@ def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
     """Compile every source and link libattn.so; returns its path."""
     extra = list(extra_flags or [])
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 5)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -1,4 +1,5 @@
-// Backward attention on bf16 MFMA (float32 accumulation), three kernels:
+// Backward attention on bf16 MFMA (float32 accumulation): the preprocess
+// and dK/dV kernels (the dQ pass is in attn_bwd_dq_bf16.hip).
 //
 //  1. preprocess: D_i = rowsum(dO o O)_i, the cheap form of rowsum(dP o P)
 //     (step-by-step derivation, "Gradient of S"; mlgrind "Follow-up"), and
@@ -6,16 +7,12 @@
 //  2. dK/dV: one workgroup per 128 keys of a head (32 per wave); it walks
 //     the query tiles, recomputes S = Q K^T and P, and accumulates
 //     dV += P^T dO and dK += dS^T Q in registers (eulerpad P2, P6).
-//  3. dQ: one workgroup per 128 queries (32 per wave); it walks the key
-//     tiles, recomputes S^T, P^T, dP^T = V dO^T and dS^T, and accumulates
-//     dQ^T += K^T dS^T (eulerpad P5).  A separate pass costs three extra
-//     products per tile pair but needs no atomics and is deterministic.
 //
 // In kernel 2 the lane owns a key: the accumulator layout of S (rows =
 // queries, columns = keys) is exactly the A-operand layout P^T and dS^T
 // need (rows = keys, k = queries), so P and dS never leave registers; the
-// partners dO and Q are read from transposed LDS copies in the matching
-// row-of-C order.  Kernel 3 mirrors this with the lane owning a query.
+// partners dO and Q are read with transposing LDS reads in the matching
+// row-of-C order.
 // The causal mask (S_ij = -inf for j > i, i.e. P_ij = 0, eulerpad P8) is
 // applied only in tiles that straddle the diagonal; tiles entirely above
 // it are never visited.
@@ -307,210 +304,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 }
 
-// ---------------------------------------------------------------- dQ
-
-template <int D, int DV>
-struct DqCfg {
-    static constexpr int BM = 128;           // queries per workgroup, 32 per wave
-    static constexpr int BN = 64;            // keys per step
-};
-
-template <int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ Dw, bf16* __restrict__ dq, int n, int m, int n_pad, float scale,
-    float c2) {
-    using C = DqCfg<D, DV>;
-    constexpr int BN = C::BN;
-    __shared__ __align__(1024) bf16 sK[2][BN * D];
-    __shared__ __align__(1024) bf16 sV[2][BN * DV];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 5, li = lane & 31;
-    const long bh = blockIdx.x;
-    const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-    const int i0 = qb * C::BM;
-    const int myq = i0 + 32 * wave + li;
-
-    const bf16* qh = q + bh * (long)n * D;
-    const bf16* kh = k + bh * (long)m * D;
-    const bf16* vh = v + bh * (long)m * DV;
-    const bf16* oh = dout + bh * (long)n * DV;
-
-    // This lane's query row: B operand of S^T = K Q^T and dP^T = V dO^T.
-    bf16x8 qreg[D / 16], oreg[DV / 16];
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-        qreg[kc] = myq < n ? gload_bf16x8(qh + (long)myq * D + 16 * kc + 8 * g) : bf16x8{};
-#pragma unroll
-    for (int kc = 0; kc < DV / 16; ++kc)
-        oreg[kc] = myq < n ? gload_bf16x8(oh + (long)myq * DV + 16 * kc + 8 * g) : bf16x8{};
-    const float l2 = lse2[bh * (long)n_pad + myq];
-    const float Dq = Dw[bh * (long)n_pad + myq];
-
-    TileOffsets<D> toK;
-    toK.init(lane);
-    TileOffsets<DV> toV;
-    toV.init(lane);
-
-    const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
-    const int nsteps = (k_end + BN - 1) / BN;
-    // Leading steps that need no mask: entirely below the diagonal and
-    // entirely inside the m keys.  The rest (at the end) are masked.
-    int n_plain = min(nsteps, m / BN);
-    if (CAUSAL) n_plain = min(n_plain, i0 / BN);
-
-    // Key rows past m repeat row m-1; masked steps zero their P.
-    auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
-        tile_load_split<D, BN, 4>(sK[buf], kh, k0, m, wave, lane);
-        tile_load_split<DV, BN, 4>(sV[buf], vh, k0, m, wave, lane);
-    };
-
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = zero16();
-
-    // One key tile: products one per slot,
-    //   A ops (per 32-key half t): S^T[t] += K_t Q^T (D/16), dP^T[t] += V_t dO^T (DV/16)
-    //   C ops (per t, c):          dQ^T += K^T dS^T (D/32)
-    // with operand reads PD slots ahead and the softmax of one half spread
-    // over the other half's products (see the dK/dV kernel).
-    auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
-        constexpr bool MASKED = decltype(masked_)::value;
-        const bf16* Ks = sK[buf];
-        const bf16* Vs = sV[buf];
-
-        constexpr int KA = D / 16, KB = DV / 16;
-        constexpr int NAT = KA + KB, NA = 2 * NAT;
-        constexpr int NCT = 2 * (D / 32), NC = 2 * NCT;
-        constexpr int NOPS = NA + NC;
-        constexpr int PD = 4;
-
-        auto load_op = [&](auto oc_) __attribute__((always_inline)) -> bf16x8 {
-            constexpr int o = decltype(oc_)::value;
-            if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
-                if constexpr (r < KA) return tile_read8_at<D>(Ks, toK, 32 * t, r);
-                else return tile_read8_at<DV>(Vs, toV, 32 * t, r - KA);
-            } else {
-                constexpr int oc = o - NA;
-                constexpr int t = oc / NCT, rc = oc % NCT;
-                constexpr int c = rc / (D / 32), x = rc % (D / 32);
-                return tile_read_tr_at<D>(Ks, toK, 32 * t + 16 * c, x);
-            }
-        };
-
-        f32x16 S[2], dP[2];
-        bf16x8 dSb[2][2];
-        float ds[16];
-        // dS^T for accumulator slot E of half T (key k0 + 32T + 8(E>>2) + 4g
-        // + (E&3)); after slots 7 and 15 the eight values become one bf16
-        // operand.
-        auto softmax_elem = [&](auto t_, auto e_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, e = decltype(e_)::value;
-            float pv = fast_exp2(__builtin_fmaf(S[t][e], c2, -l2));
-            if constexpr (MASKED) {
-                const int key = k0 + 32 * t + 8 * (e >> 2) + 4 * g + (e & 3);
-                pv = (key >= m || (CAUSAL && key > myq)) ? 0.f : pv;
-            }
-            ds[e] = pv * (dP[t][e] - Dq);
-            if constexpr ((e & 7) == 7) {
-                constexpr int c = e >> 3, b = 8 * c;
-                dSb[t][c] = pack8(ds[b], ds[b + 1], ds[b + 2], ds[b + 3], ds[b + 4], ds[b + 5],
-                                  ds[b + 6], ds[b + 7]);
-            }
-        };
-        // Softmax windows as in the dK/dV kernel: half 0 over the A ops of
-        // half 1, half 1 over the C ops of half 0.
-        constexpr int W0[2] = {NAT + 2, NA + 1};
-        constexpr int W1[2] = {NA, NA + NCT + (D / 32) - 1};
-        static_assert(W1[0] > W0[0] && W1[1] > W0[1], "softmax windows");
-        static_assert(W0[1] + (7 * (W1[1] - W0[1])) / 16 < NA + NCT, "half 1 low operand in time");
-
-        bf16x8 fr[PD];
-        static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
-        __builtin_amdgcn_sched_barrier(0);
-
-        static_for<NOPS>([&](auto o_) {
-            constexpr int o = decltype(o_)::value;
-            const bf16x8 cur = fr[o % PD];
-            if constexpr (o + PD < NOPS)
-                fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
-            if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
-                if constexpr (o % NAT == 0) {
-                    S[t] = zero16();
-                    dP[t] = zero16();
-                }
-                if constexpr (r < KA) S[t] = mfma32(cur, qreg[r], S[t]);
-                else dP[t] = mfma32(cur, oreg[r - KA], dP[t]);
-            } else {
-                constexpr int oc = o - NA;
-                constexpr int t = oc / NCT, rc = oc % NCT;
-                constexpr int c = rc / (D / 32), x = rc % (D / 32);
-                acc[x] = mfma32(cur, dSb[t][c], acc[x]);
-            }
-            static_for<2>([&](auto t_) {
-                constexpr int t = decltype(t_)::value;
-                constexpr int L = W1[t] - W0[t];
-                static_for<16>([&](auto e_) {
-                    constexpr int e = decltype(e_)::value;
-                    if constexpr (W0[t] + (e * L) / 16 == o) softmax_elem(t_, e_);
-                });
-            });
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
-    auto do_step = [&](auto buf_, auto masked_, int s) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
-        const int k0 = s * BN;
-        if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, k0 + BN);
-        compute(buf_, masked_, k0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    };
-
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    using MaskOn = std::integral_constant<bool, true>;
-    using MaskOff = std::integral_constant<bool, false>;
-
-    if (nsteps > 0) stage(B0{}, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    int s = 0;
-    for (; s + 1 < n_plain; s += 2) {
-        do_step(B0{}, MaskOff{}, s);
-        do_step(B1{}, MaskOff{}, s + 1);
-    }
-    if (s < n_plain) do_step(B0{}, MaskOff{}, s++);
-    for (; s < nsteps; ++s) {
-        if (s & 1) do_step(B1{}, MaskOn{}, s);
-        else do_step(B0{}, MaskOn{}, s);
-    }
-
-    // Accumulator slot vv of tile mt holds column d = 32*mt + 8*(vv>>2) + 4g + (vv&3)
-    // of this lane's query.
-    if (myq < n) {
-        bf16* qrow = dq + (bh * (long)n + myq) * D;
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) {
-#pragma unroll
-            for (int vq = 0; vq < 4; ++vq) {
-                bf16x4 w;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[mt][4 * vq + r] * scale);
-                *reinterpret_cast<bf16x4*>(qrow + 32 * mt + 8 * vq + 4 * g) = w;
-            }
-        }
-    }
-}
-
 template <int DV>
 void launch_pre(const Problem& p, const void* o, const void* dout, const float* lse,
                 const Workspace& w, hipStream_t s) {
@@ -537,22 +330,6 @@ void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
             (bf16*)dk, (bf16*)dv, p.n, p.m, w.n_pad, p.scale, c2);
 }
 
-template <int D, int DV>
-void launch_dq(const Problem& p, const void* q, const void* k, const void* v, const void* dout,
-               const Workspace& w, void* dq, hipStream_t s) {
-    using C = DqCfg<D, DV>;
-    dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
-    const float c2 = p.scale * kLog2e;
-    if (p.causal)
-        bwd_dq_kernel<D, DV, true><<<grid, 256, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
-            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
-    else
-        bwd_dq_kernel<D, DV, false><<<grid, 256, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
-            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
-}
-
 }  // namespace
 
 bool launch_bwd_preprocess_bf16(const Problem& p, const void* o, const void* dout,
@@ -569,15 +346,6 @@ bool launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const 
     if (p.d == 64 && p.dv == 64) launch_dkdv<64, 64>(p, q, k, v, dout, w, dk, dv, s);
     else if (p.d == 128 && p.dv == 128) launch_dkdv<128, 128>(p, q, k, v, dout, w, dk, dv, s);
     else if (p.d == 128 && p.dv == 64) launch_dkdv<128, 64>(p, q, k, v, dout, w, dk, dv, s);
-    else return false;
-    return true;
-}
-
-bool launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
-                        const void* dout, const Workspace& w, void* dq, hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch_dq<64, 64>(p, q, k, v, dout, w, dq, s);
-    else if (p.d == 128 && p.dv == 128) launch_dq<128, 128>(p, q, k, v, dout, w, dq, s);
-    else if (p.d == 128 && p.dv == 64) launch_dq<128, 64>(p, q, k, v, dout, w, dq, s);
     else return false;
     return true;
 }

@@ -1,0 +1,295 @@
+// dQ of backward attention on bf16 MFMA (float32 accumulation).
+//
+// For query row i, dQ_i = scale * sum_j dS_ij K_j with dS = P o (dP - D)
+// and dP = dO V^T ("Attention Backpropagation: Step by step derivation",
+// sections Gradient of S and Gradient of Q and K; mlgrind "Backward";
+// eulerpad P5).  This pass recomputes S, P and dP per key tile instead of
+// reading a stored P, and needs no atomics: each workgroup owns its query
+// rows and walks the keys.
+//
+// Layout: one workgroup per 256 queries of a head, four waves, each wave
+// owning two 32-query MFMA tiles.  The lane owns a query column of the
+// transposed products
+//     S^T = K Q^T,   dP^T = V dO^T,   dQ^T += K^T dS^T,
+// so this lane's rows of Q and dO are register-resident B operands, and
+// the accumulator layout of dS^T (rows = keys) is the B operand of the dQ
+// product in row-of-C order (see attn_device.h).  Every 32-key tile of K
+// and V is staged once in LDS and each fragment read from it feeds two
+// MFMAs, one per query tile of the wave.  The causal mask (S_ij = -inf for
+// j > i, i.e. P_ij = 0, eulerpad P8) is applied only in key tiles that
+// reach past the workgroup's first query.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+template <int D, int DV>
+struct DqCfg {
+    static constexpr int NW = 4;              // waves per workgroup
+    static constexpr int BM = 2 * 32 * NW;    // queries per workgroup
+    static constexpr int BN = 32;             // keys per step
+    static constexpr int PD = 4;              // operand reads issued ahead
+};
+
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ Dw, bf16* __restrict__ dq, int n, int m, int n_pad, float scale,
+    float c2) {
+    using C = DqCfg<D, DV>;
+    constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
+    __shared__ __align__(1024) bf16 sK[2][BN * D];
+    __shared__ __align__(1024) bf16 sV[2][BN * DV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, li = lane & 31;
+    const long bh = blockIdx.x;
+    const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+    const int i0 = qb * C::BM;
+
+    const bf16* qh = q + bh * (long)n * D;
+    const bf16* kh = k + bh * (long)m * D;
+    const bf16* vh = v + bh * (long)m * DV;
+    const bf16* oh = dout + bh * (long)n * DV;
+
+    // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31).
+    // Taking one tile from each half of the workgroup's rows gives every
+    // wave the same share of the masked diagonal work.  Rows past n load
+    // zeros and LSE2 = +inf, so their P, dS and dQ contributions vanish.
+    int myq[2];
+    bf16x8 qreg[2][D / 16], oreg[2][DV / 16];
+    float l2[2], Dq[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        myq[t] = i0 + (C::BM / 2) * t + 32 * wave + li;
+        const bool ok = myq[t] < n;
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc)
+            qreg[t][kc] = ok ? gload_bf16x8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : bf16x8{};
+#pragma unroll
+        for (int kc = 0; kc < DV / 16; ++kc)
+            oreg[t][kc] = ok ? gload_bf16x8(oh + (long)myq[t] * DV + 16 * kc + 8 * g) : bf16x8{};
+        l2[t] = ok ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
+        Dq[t] = ok ? Dw[bh * (long)n_pad + myq[t]] : 0.f;
+    }
+
+    TileOffsets<D> toK;
+    toK.init(lane);
+    TileOffsets<DV> toV;
+    toV.init(lane);
+
+    const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
+    const int nsteps = (k_end + BN - 1) / BN;
+    // Leading steps that need no mask: every key below the workgroup's
+    // first query (causal) and inside the m keys.  The rest are masked.
+    int n_plain = min(nsteps, m / BN);
+    if (CAUSAL) n_plain = min(n_plain, i0 / BN);
+
+    // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead.
+    // Rows past m (last tile only) repeat row m-1; masked steps zero their P.
+    TileLoader<D, BN, NW> ldK;
+    ldK.init(wave, lane);
+    TileLoader<DV, BN, NW> ldV;
+    ldV.init(wave, lane);
+    auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
+        constexpr int buf = decltype(buf_)::value;
+        if (k0 + BN <= m) {
+            tile_fill<D, BN, NW>(ldK, sK[buf], kh, k0, wave);
+            tile_fill<DV, BN, NW>(ldV, sV[buf], vh, k0, wave);
+        } else {
+            tile_fill_clamped<D, BN, NW>(ldK, sK[buf], kh, k0, m, wave, lane);
+            tile_fill_clamped<DV, BN, NW>(ldV, sV[buf], vh, k0, m, wave, lane);
+        }
+    };
+
+    f32x16 acc[D / 32][2];
+#pragma unroll
+    for (int x = 0; x < D / 32; ++x) {
+        acc[x][0] = zero16();
+        acc[x][1] = zero16();
+    }
+
+    // One key tile as a fixed sequence of operand fragments, each read once
+    // from LDS and used by two MFMAs (query tiles 0 and 1):
+    //   f <  KA:            K rows, d chunk f        -> S^T[t]  += K Q_t^T
+    //   f <  KA + KB:       V rows, dv chunk f - KA  -> dP^T[t] += V dO_t^T
+    //   f <  KA + KB + 2NX: K^T, key half c, d block x -> dQ^T[x][t] += K^T dS^T[t]
+    // P = exp2(S * scale * log2e - LSE2) is formed during the dP products,
+    // dS = P (dP - D) for key half 0 right after them and for key half 1
+    // during the half-0 dQ products.
+    auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
+        constexpr int buf = decltype(buf_)::value;
+        constexpr bool MASKED = decltype(masked_)::value;
+        const bf16* Ks = sK[buf];
+        const bf16* Vs = sV[buf];
+        constexpr int KA = D / 16, KB = DV / 16, NX = D / 32;
+        constexpr int NF = KA + KB + 2 * NX;
+
+        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
+            constexpr int f = decltype(f_)::value;
+            if constexpr (f < KA) {
+                return tile_read8_at<D>(Ks, toK, 0, f);
+            } else if constexpr (f < KA + KB) {
+                return tile_read8_at<DV>(Vs, toV, 0, f - KA);
+            } else {
+                constexpr int cx = f - KA - KB, c = cx / NX, x = cx % NX;
+                return tile_read_tr_at<D>(Ks, toK, 16 * c, x);
+            }
+        };
+
+        f32x16 S[2], dP[2];
+        bf16x8 dSb[2][2];
+
+        // P for accumulator slot e of tile t, written over S.  The slot's key
+        // is k0 + 4g + kr(e), kr(e) = 8(e>>2) + (e&3); it is visible when
+        // kr(e) <= lim[t] (key < m and, causal, key <= query).
+        int lim[2];
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                lim[t] = m - 1 - k0 - 4 * g;
+                if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] - k0 - 4 * g);
+            }
+        }
+        auto p_elem = [&](auto t_, auto e_) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_)::value, e = decltype(e_)::value;
+            float pv = fast_exp2(__builtin_fmaf(S[t][e], c2, -l2[t]));
+            if constexpr (MASKED) pv = (8 * (e >> 2) + (e & 3) > lim[t]) ? 0.f : pv;
+            S[t][e] = pv;
+        };
+        // dS for key half c of tile t, as one bf16 operand (row-of-C order).
+        auto ds_half = [&](auto t_, auto c_) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_)::value, c = decltype(c_)::value;
+            float d8[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) d8[s] = S[t][8 * c + s] * (dP[t][8 * c + s] - Dq[t]);
+            dSb[t][c] = pack8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
+        };
+
+        bf16x8 fr[PD];
+        static_for<PD>([&](auto f_) { fr[decltype(f_)::value] = load_frag(f_); });
+        __builtin_amdgcn_sched_barrier(0);
+
+        static_for<NF>([&](auto f_) {
+            constexpr int f = decltype(f_)::value;
+            const bf16x8 cur = fr[f % PD];
+            if constexpr (f + PD < NF) fr[f % PD] = load_frag(std::integral_constant<int, f + PD>{});
+            if constexpr (f < KA) {
+                static_for<2>([&](auto t_) {
+                    constexpr int t = decltype(t_)::value;
+                    if constexpr (f == 0) S[t] = zero16();
+                    S[t] = mfma32(cur, qreg[t][f], S[t]);
+                });
+            } else if constexpr (f < KA + KB) {
+                constexpr int r = f - KA;
+                static_for<2>([&](auto t_) {
+                    constexpr int t = decltype(t_)::value;
+                    if constexpr (r == 0) dP[t] = zero16();
+                    dP[t] = mfma32(cur, oreg[t][r], dP[t]);
+                });
+                // 32 exponentials (two tiles x 16 slots) over the KB dP slots
+                static_for<32>([&](auto i_) {
+                    constexpr int i = decltype(i_)::value;
+                    if constexpr ((i * KB) / 32 == r)
+                        p_elem(std::integral_constant<int, i / 16>{}, std::integral_constant<int, i % 16>{});
+                });
+                if constexpr (r == KB - 1) {
+                    ds_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+                    ds_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+                }
+            } else {
+                constexpr int cx = f - KA - KB, c = cx / NX, x = cx % NX;
+                static_for<2>([&](auto t_) {
+                    constexpr int t = decltype(t_)::value;
+                    acc[x][t] = mfma32(cur, dSb[t][c], acc[x][t]);
+                });
+                if constexpr (c == 0 && x == 0)
+                    ds_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+                if constexpr (c == 0 && x == (NX > 1 ? 1 : 0))
+                    ds_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using MaskOn = std::integral_constant<bool, true>;
+    using MaskOff = std::integral_constant<bool, false>;
+
+    auto do_step = [&](auto buf_, auto masked_, int s) __attribute__((always_inline)) {
+        constexpr int buf = decltype(buf_)::value;
+        const int k0 = s * BN;
+        if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, k0 + BN);
+        compute(buf_, masked_, k0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    if (nsteps > 0) stage(B0{}, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Both loops start on buffer 0: an odd plain step joins the masked ones.
+    const int n_plain2 = n_plain & ~1;
+    int s = 0;
+    for (; s < n_plain2; s += 2) {
+        do_step(B0{}, MaskOff{}, s);
+        do_step(B1{}, MaskOff{}, s + 1);
+    }
+    for (; s + 1 < nsteps; s += 2) {
+        do_step(B0{}, MaskOn{}, s);
+        do_step(B1{}, MaskOn{}, s + 1);
+    }
+    if (s < nsteps) do_step(B0{}, MaskOn{}, s);
+
+    // Accumulator slot vv of tile (x, t) holds column d = 32x + 8(vv>>2) +
+    // 4g + (vv&3) of query myq[t].
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (myq[t] < n) {
+            bf16* qrow = dq + (bh * (long)n + myq[t]) * D;
+#pragma unroll
+            for (int x = 0; x < D / 32; ++x) {
+#pragma unroll
+                for (int vq = 0; vq < 4; ++vq) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[x][t][4 * vq + r] * scale);
+                    *reinterpret_cast<bf16x4*>(qrow + 32 * x + 8 * vq + 4 * g) = w;
+                }
+            }
+        }
+    }
+}
+
+template <int D, int DV>
+void launch_dq(const Problem& p, const void* q, const void* k, const void* v, const void* dout,
+               const Workspace& w, void* dq, hipStream_t s) {
+    using C = DqCfg<D, DV>;
+    dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
+    const float c2 = p.scale * kLog2e;
+    if (p.causal)
+        bwd_dq_kernel<D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
+            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+    else
+        bwd_dq_kernel<D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
+            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+}
+
+}  // namespace
+
+bool launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                        const void* dout, const Workspace& w, void* dq, hipStream_t s) {
+    if (p.d == 64 && p.dv == 64) launch_dq<64, 64>(p, q, k, v, dout, w, dq, s);
+    else if (p.d == 128 && p.dv == 128) launch_dq<128, 128>(p, q, k, v, dout, w, dq, s);
+    else if (p.d == 128 && p.dv == 64) launch_dq<128, 64>(p, q, k, v, dout, w, dq, s);
+    else return false;
+    return true;
+}
+
+}  // namespace attn

@@ -223,6 +223,54 @@ __device__ __forceinline__ void tile_load_split(bf16* lds_tile, const bf16* g, i
     }
 }
 
+// The tile_load_split pattern with the per-lane source offsets computed
+// once: load jj of wave w fills kilobyte ii = w + NW*jj of the tile, this
+// lane fetching chunk s ^ swz(r) of tile row r (p = 64 ii + lane, r = p /
+// CPR, s = p % CPR); off[jj] is that chunk's element offset from the
+// tile's first global row.
+template <int C, int ROWS, int NW>
+struct TileLoader {
+    using T = SwzTile<C>;
+    static constexpr int N = ROWS * T::CPR / 64 / NW;
+    static_assert(N * 64 * NW == ROWS * T::CPR, "tile loads must split evenly over the waves");
+    int off[N];
+    __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+        for (int jj = 0; jj < N; ++jj) {
+            const int p = (w + NW * jj) * 64 + lane;
+            const int r = p / T::CPR, s = p % T::CPR;
+            off[jj] = r * C + 8 * (s ^ T::swz(r));
+        }
+    }
+};
+
+// Fill a tile from rows row0 .. row0 + ROWS - 1 of g, all inside the matrix.
+template <int C, int ROWS, int NW>
+__device__ __forceinline__ void tile_fill(const TileLoader<C, ROWS, NW>& L, bf16* lds_tile,
+                                          const bf16* g, int row0, int w) {
+    const bf16* base = g + (long)row0 * C;
+#pragma unroll
+    for (int jj = 0; jj < TileLoader<C, ROWS, NW>::N; ++jj) {
+        const bf16* src = base + L.off[jj];
+        __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + (w + NW * jj) * 512), 16, 0, 0);
+    }
+}
+
+// As tile_fill, but rows at or past `valid` read row valid-1 instead.
+template <int C, int ROWS, int NW>
+__device__ __forceinline__ void tile_fill_clamped(const TileLoader<C, ROWS, NW>& L, bf16* lds_tile,
+                                                  const bf16* g, int row0, int valid, int w,
+                                                  int lane) {
+    using T = SwzTile<C>;
+#pragma unroll
+    for (int jj = 0; jj < TileLoader<C, ROWS, NW>::N; ++jj) {
+        const int r = ((w + NW * jj) * 64 + lane) / T::CPR;
+        const int grow = row0 + r < valid ? row0 + r : valid - 1;
+        const bf16* src = g + (long)grow * C + (L.off[jj] - r * C);
+        __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + (w + NW * jj) * 512), 16, 0, 0);
+    }
+}
+
 // One of the INSTS/NW loads tile_load_split would issue (number jj), so
 // that a tile's loads can be spread over a step instead of issued at once.
 template <int C, int ROWS, int NW>
