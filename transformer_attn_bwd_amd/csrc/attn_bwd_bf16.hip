@@ -78,10 +78,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     int n_pad, float scale, float c2) {
     using C = DkdvCfg<D, DV>;
     constexpr int BM = C::BM;
-    __shared__ __align__(1024) bf16 sQ[2][BM * D];
-    __shared__ __align__(1024) bf16 sO[2][BM * DV];
-    __shared__ __align__(256) float sL[2][BM];
-    __shared__ __align__(256) float sD[2][BM];
+    // One LDS variable per buffer: the compiler can then tell that reads
+    // of one buffer do not alias the asynchronous fills of the other, and
+    // does not make them wait for those fills.
+    __shared__ __align__(1024) bf16 sQ0[BM * D];
+    __shared__ __align__(1024) bf16 sQ1[BM * D];
+    __shared__ __align__(1024) bf16 sO0[BM * DV];
+    __shared__ __align__(1024) bf16 sO1[BM * DV];
+    __shared__ __align__(256) float sL0[BM];
+    __shared__ __align__(256) float sL1[BM];
+    __shared__ __align__(256) float sD0[BM];
+    __shared__ __align__(256) float sD1[BM];
+    auto pick = [](auto b_, auto* x0, auto* x1) __attribute__((always_inline)) {
+        if constexpr (decltype(b_)::value == 0) return x0;
+        else return x1;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -115,17 +126,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int i_end = (n + BM - 1) / BM * BM;
     const int nsteps = (i_end - i_begin) / BM;
 
-    // Stage query tile i0 into buffer BUF: Q and dO rows (rows past n repeat
-    // row n-1; their LSE2 is +inf, so P = 0 and they contribute nothing),
-    // and the per-row LSE2 and D.
+    // Stage query tile i0 into a buffer: Q and dO rows (rows past n come
+    // back as zeros; their LSE2 is +inf, so P = 0 and they contribute
+    // nothing), and the per-row LSE2 and D.
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)n * D * 2);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)n * DV * 2);
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lh, (uint32_t)n_pad * 4);
+    const __amdgpu_buffer_rsrc_t rD = make_rsrc(dh, (uint32_t)n_pad * 4);
+    TileLoader<D, BM, 4> ldQ;
+    ldQ.init(wave, lane);
+    TileLoader<DV, BM, 4> ldO;
+    ldO.init(wave, lane);
     auto stage = [&](auto buf_, int i0) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
-        tile_load_split<D, BM, 4>(sQ[buf], qh, i0, n, wave, lane);
-        tile_load_split<DV, BM, 4>(sO[buf], oh, i0, n, wave, lane);
+        tile_fill<D, BM, 4>(ldQ, pick(buf_, sQ0, sQ1), rQ, i0, wave);
+        tile_fill<DV, BM, 4>(ldO, pick(buf_, sO0, sO1), rO, i0, wave);
         if (wave == 0)
-            __builtin_amdgcn_global_load_lds(lh + i0 + lane, (ATTN_LDS void*)sL[buf], 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (ATTN_LDS void*)pick(buf_, sL0, sL1), 4,
+                                                     4 * lane, 4 * i0, 0, 0);
         else if (wave == 1)
-            __builtin_amdgcn_global_load_lds(dh + i0 + lane, (ATTN_LDS void*)sD[buf], 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (ATTN_LDS void*)pick(buf_, sD0, sD1), 4,
+                                                     4 * lane, 4 * i0, 0, 0);
     };
 
     f32x16 accK[D / 32], accV[DV / 32];
@@ -144,12 +164,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // time.  Slots are fenced with sched_barrier so the compiler keeps this
     // order.  MASKED steps apply the causal mask (tiles on the diagonal).
     auto compute = [&](auto buf_, auto masked_, int i0) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
         constexpr bool MASKED = decltype(masked_)::value;
-        const bf16* Qs = sQ[buf];
-        const bf16* Os = sO[buf];
-        const float* Ls = sL[buf];
-        const float* Dsm = sD[buf];
+        const bf16* Qs = pick(buf_, sQ0, sQ1);
+        const bf16* Os = pick(buf_, sO0, sO1);
+        const float* Ls = pick(buf_, sL0, sL1);
+        const float* Dsm = pick(buf_, sD0, sD1);
 
         constexpr int KA = D / 16, KB = DV / 16;
         constexpr int NAT = KA + KB, NA = 2 * NAT;

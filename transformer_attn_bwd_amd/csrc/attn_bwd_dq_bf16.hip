@@ -40,8 +40,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     float c2) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
-    __shared__ __align__(1024) bf16 sK[2][BN * D];
-    __shared__ __align__(1024) bf16 sV[2][BN * DV];
+    // One LDS variable per buffer: the compiler can then tell that reads
+    // of one buffer do not alias the asynchronous fills of the other, and
+    // does not make them wait for those fills.
+    __shared__ __align__(1024) bf16 sK0[BN * D];
+    __shared__ __align__(1024) bf16 sK1[BN * D];
+    __shared__ __align__(1024) bf16 sV0[BN * DV];
+    __shared__ __align__(1024) bf16 sV1[BN * DV];
+    auto Kbuf = [&](auto b_) __attribute__((always_inline)) -> bf16* {
+        if constexpr (decltype(b_)::value == 0) return sK0;
+        else return sK1;
+    };
+    auto Vbuf = [&](auto b_) __attribute__((always_inline)) -> bf16* {
+        if constexpr (decltype(b_)::value == 0) return sV0;
+        else return sV1;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
@@ -88,20 +101,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if (CAUSAL) n_plain = min(n_plain, i0 / BN);
 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead.
-    // Rows past m (last tile only) repeat row m-1; masked steps zero their P.
+    // Rows past m (last tile only) come back as zeros; masked steps zero
+    // their P.
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)m * D * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)m * DV * 2);
     TileLoader<D, BN, NW> ldK;
     ldK.init(wave, lane);
     TileLoader<DV, BN, NW> ldV;
     ldV.init(wave, lane);
     auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
-        if (k0 + BN <= m) {
-            tile_fill<D, BN, NW>(ldK, sK[buf], kh, k0, wave);
-            tile_fill<DV, BN, NW>(ldV, sV[buf], vh, k0, wave);
-        } else {
-            tile_fill_clamped<D, BN, NW>(ldK, sK[buf], kh, k0, m, wave, lane);
-            tile_fill_clamped<DV, BN, NW>(ldV, sV[buf], vh, k0, m, wave, lane);
-        }
+        tile_fill<D, BN, NW>(ldK, Kbuf(buf_), rK, k0, wave);
+        tile_fill<DV, BN, NW>(ldV, Vbuf(buf_), rV, k0, wave);
     };
 
     f32x16 acc[D / 32][2];
@@ -120,10 +130,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // dS = P (dP - D) for key half 0 right after them and for key half 1
     // during the half-0 dQ products.
     auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
-        constexpr int buf = decltype(buf_)::value;
         constexpr bool MASKED = decltype(masked_)::value;
-        const bf16* Ks = sK[buf];
-        const bf16* Vs = sV[buf];
+        const bf16* Ks = Kbuf(buf_);
+        const bf16* Vs = Vbuf(buf_);
         constexpr int KA = D / 16, KB = DV / 16, NX = D / 32;
         constexpr int NF = KA + KB + 2 * NX;
 

@@ -244,31 +244,25 @@ struct TileLoader {
     }
 };
 
-// Fill a tile from rows row0 .. row0 + ROWS - 1 of g, all inside the matrix.
-template <int C, int ROWS, int NW>
-__device__ __forceinline__ void tile_fill(const TileLoader<C, ROWS, NW>& L, bf16* lds_tile,
-                                          const bf16* g, int row0, int w) {
-    const bf16* base = g + (long)row0 * C;
-#pragma unroll
-    for (int jj = 0; jj < TileLoader<C, ROWS, NW>::N; ++jj) {
-        const bf16* src = base + L.off[jj];
-        __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + (w + NW * jj) * 512), 16, 0, 0);
-    }
+// Buffer resource for a raw byte range [base, base + bytes): loads through
+// it at offsets past the end return zeros (the fourth descriptor word
+// selects 32-bit raw data, the usual value for untyped buffer access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
-// As tile_fill, but rows at or past `valid` read row valid-1 instead.
+// Fill a tile from rows row0 .. row0 + ROWS - 1 of the [*, C] bf16 matrix
+// behind `rsrc` (buffer loads straight into LDS); rows past the end of the
+// buffer come back as zeros.
 template <int C, int ROWS, int NW>
-__device__ __forceinline__ void tile_fill_clamped(const TileLoader<C, ROWS, NW>& L, bf16* lds_tile,
-                                                  const bf16* g, int row0, int valid, int w,
-                                                  int lane) {
-    using T = SwzTile<C>;
+__device__ __forceinline__ void tile_fill(const TileLoader<C, ROWS, NW>& L, bf16* lds_tile,
+                                          __amdgpu_buffer_rsrc_t rsrc, int row0, int w) {
 #pragma unroll
-    for (int jj = 0; jj < TileLoader<C, ROWS, NW>::N; ++jj) {
-        const int r = ((w + NW * jj) * 64 + lane) / T::CPR;
-        const int grow = row0 + r < valid ? row0 + r : valid - 1;
-        const bf16* src = g + (long)grow * C + (L.off[jj] - r * C);
-        __builtin_amdgcn_global_load_lds(src, (ATTN_LDS void*)(lds_tile + (w + NW * jj) * 512), 16, 0, 0);
-    }
+    for (int jj = 0; jj < TileLoader<C, ROWS, NW>::N; ++jj)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (ATTN_LDS void*)(lds_tile + (w + NW * jj) * 512),
+                                                 16, (unsigned)(2 * L.off[jj]),
+                                                 (unsigned)(2 * row0 * C), 0, 0);
 }
 
 // One of the INSTS/NW loads tile_load_split would issue (number jj), so
