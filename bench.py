@@ -26,6 +26,34 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the backward kernels on causal_4k_d128, from
+# rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the
+# same counters read for a plain 1 GiB device copy (x2.0 and x1.0).  They
+# hold only for the kernel sources they were taken on, identified by hash;
+# after any change to those sources the traffic is reported as null.
+KERNEL_SOURCES = ("attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_device.h", "attn_launch.h")
+MEASURED_TRAFFIC = {
+    "workload": "causal_4k_d128",
+    "sources_sha256": "b1b9fca4b436b2ecfd15eb4520178b6e5679462481a78a95ae4aa043850331da",
+    "bytes": {"bwd_dkdv": 8.78e+08, "bwd_dq": 6.254e+08},
+}
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_attn_bwd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    m = MEASURED_TRAFFIC
+    if m["workload"] != workload or m["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return m["bytes"].get(kernel)
+
 
 def bwd_flops(w) -> float:
     f = 2.0 * w.n * w.m * (3 * w.d + 2 * w.dv) * w.B * w.H
@@ -208,7 +236,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name, f"bwd_{dominant}"),
         },
         "dkdv_tflops": round(dk_tf, 2),
         "hbm_algorithmic_GBps": round(bwd_bytes(w) / (ms * 1e-3) / 1e9, 1),
