@@ -4,7 +4,7 @@
 //  1. preprocess: D_i = rowsum(dO o O)_i, the cheap form of rowsum(dP o P)
 //     (step-by-step derivation, "Gradient of S"; mlgrind "Follow-up"), and
 //     LSE rescaled to base 2 so that P = exp2(S * scale * log2e - LSE2).
-//  2. dK/dV: one workgroup per 128 keys of a head (32 per wave); it walks
+//  2. dK/dV: one workgroup per 256 keys of a head (64 per wave); it walks
 //     the query tiles, recomputes S = Q K^T and P, and accumulates
 //     dV += P^T dO and dK += dS^T Q in registers (eulerpad P2, P6).
 //
@@ -21,16 +21,6 @@
 
 namespace attn {
 namespace {
-
-// Order of the S and dP products within a query (or key) half: the two
-// accumulation chains alternate so that consecutive products never depend
-// on each other; the longer chain's remainder goes last.
-template <int KA, int KB>
-constexpr int a_order(int r0) {
-    constexpr int m = KA < KB ? KA : KB;
-    if (r0 < 2 * m) return (r0 & 1) ? KA + r0 / 2 : r0 / 2;
-    return KA > KB ? (r0 - m) : (KA + (r0 - m));
-}
 
 // ---------------------------------------------------------------- preprocess
 
@@ -66,10 +56,66 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
 
 template <int D, int DV>
 struct DkdvCfg {
-    static constexpr int BN = 128;           // keys per workgroup, 32 per wave
-    static constexpr int BM = 64;            // queries per step
+    static constexpr int NW = 4;             // waves per workgroup
+    static constexpr int KW = 64;            // keys per wave (two 32-key MFMA tiles)
+    static constexpr int BN = NW * KW;       // keys per workgroup
+    static constexpr int BM = 32;            // queries per step
+    static constexpr int LA = 4;             // operand reads issued this many MFMAs ahead
 };
 
+// Per-step schedule of the dK/dV kernel, all compile-time.  With KA = D/16,
+// KB = DV/16, NX = D/32, NXV = DV/32 the step issues, in order,
+//   S    2KA MFMAs  j = 2r + kt          S[kt]  += Q_r  K[kt]_r^T
+//   dP   2KB MFMAs  j = 2KA + 2r + kt    dP[kt] += dO_r V[kt]_r^T
+//   dV  4NXV MFMAs  2(c NXV + x) + kt    dV[kt][x] += P[kt]^T_c dO_c,x
+//   dK  4NX  MFMAs  2(c NX + x) + kt     dK[kt][x] += dS[kt]^T_c Q_c,x
+// (kt: 32-key tile of the wave, r: 16-wide chunk of d or dv, c: 16-query
+// half of the step, x: 32-column block).  Operand fragments read from LDS:
+//   f <  KA               Q rows, chunk f              (first used by j = 2f)
+//   f < 3KA               K rows of tile kt, chunk r   (j = 2r + kt)
+//   f < 3KA + KB          dO rows, chunk r             (j = 2KA + 2r)
+//   f < 3KA + KB + 2NXV   dO^T half c, block x         (dV, first j of (c, x))
+//   f < 3KA + KB + 2NXV + 2NX   Q^T half c, block x    (dK, first j of (c, x))
+template <int D, int DV>
+struct DkdvSched {
+    static constexpr int KA = D / 16, KB = DV / 16, NX = D / 32, NXV = DV / 32;
+    static constexpr int J_DP = 2 * KA, J_DV = J_DP + 2 * KB, J_DK = J_DV + 4 * NXV;
+    static constexpr int NJ = J_DK + 4 * NX;
+    static constexpr int F_K = KA, F_DO = 3 * KA, F_DOT = F_DO + KB, F_QT = F_DOT + 2 * NXV;
+    static constexpr int NF = F_QT + 2 * NX;
+    static constexpr int first_use(int f) {
+        if (f < F_K) return 2 * f;
+        if (f < F_DO) return 2 * ((f - F_K) % KA) + (f - F_K) / KA;
+        if (f < F_DOT) return J_DP + 2 * (f - F_DO);
+        if (f < F_QT) return J_DV + 2 * (f - F_DOT);
+        return J_DK + 2 * (f - F_QT);
+    }
+    static constexpr int issue_at(int f, int la) {
+        return first_use(f) - la < 0 ? 0 : first_use(f) - la;
+    }
+    // Softmax elements, 32 per step per lane: element i is accumulator
+    // slot e(i) of key tile kt(i); ordered by 8-slot operand chunk, so
+    // that each bf16 operand is complete early.
+    static constexpr int elem_c(int i) { return i / 16; }
+    static constexpr int elem_kt(int i) { return (i / 8) % 2; }
+    static constexpr int elem_e(int i) { return 8 * elem_c(i) + i % 8; }
+    // P = exp2(...) of element i is formed in dP slot p_slot(i), dS in dV
+    // slot ds_slot(i).
+    static constexpr int p_slot(int i) { return J_DP + (i * 2 * KB) / 32; }
+    static constexpr int ds_slot(int i) { return J_DV + (i * 4 * NXV) / 32; }
+    // statistics of row group vq (accumulator slots 4vq..4vq+3) are read
+    // two slots before the first element that needs them
+    static constexpr int first_elem_of_vq(int vq) { return 16 * (vq / 2) + 4 * (vq % 2); }
+    static constexpr int l_slot(int vq) { return p_slot(first_elem_of_vq(vq)) - 2; }
+    static constexpr int d_slot(int vq) { return ds_slot(first_elem_of_vq(vq)) - 2; }
+};
+
+// One workgroup per 256 keys of a head, four waves of 64 keys.  The
+// workgroup's K rows sit in LDS for the whole kernel and this wave's V rows
+// in registers (B operands of S = Q K^T and dP = dO V^T, lane = key); the
+// query tiles (32 rows of Q and dO, with their LSE2 and D) stream through
+// two LDS buffers.  Each Q, dO, Q^T and dO^T fragment read from LDS feeds
+// two MFMAs (the wave's two key tiles).  dK and dV accumulate in AGPRs.
 template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -77,18 +123,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const float* __restrict__ Dw, bf16* __restrict__ dk, bf16* __restrict__ dvo, int n, int m,
     int n_pad, float scale, float c2) {
     using C = DkdvCfg<D, DV>;
-    constexpr int BM = C::BM;
+    using SC = DkdvSched<D, DV>;
+    constexpr int BM = C::BM, NW = C::NW, LA = C::LA;
     // One LDS variable per buffer: the compiler can then tell that reads
     // of one buffer do not alias the asynchronous fills of the other, and
     // does not make them wait for those fills.
+    __shared__ __align__(1024) bf16 sK[C::BN * D];
     __shared__ __align__(1024) bf16 sQ0[BM * D];
     __shared__ __align__(1024) bf16 sQ1[BM * D];
     __shared__ __align__(1024) bf16 sO0[BM * DV];
     __shared__ __align__(1024) bf16 sO1[BM * DV];
-    __shared__ __align__(256) float sL0[BM];
-    __shared__ __align__(256) float sL1[BM];
-    __shared__ __align__(256) float sD0[BM];
-    __shared__ __align__(256) float sD1[BM];
+    __shared__ __align__(256) float sL0[64];
+    __shared__ __align__(256) float sL1[64];
+    __shared__ __align__(256) float sD0[64];
+    __shared__ __align__(256) float sD1[64];
     auto pick = [](auto b_, auto* x0, auto* x1) __attribute__((always_inline)) {
         if constexpr (decltype(b_)::value == 0) return x0;
         else return x1;
@@ -98,8 +146,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int g = lane >> 5, li = lane & 31;
     const long bh = blockIdx.x;
     const int j0 = blockIdx.y * C::BN;
-    const int kw0 = j0 + 32 * wave;
-    const int myk = kw0 + li;
+    const int kw0 = j0 + C::KW * wave;      // this wave's first key
 
     const bf16* qh = q + bh * (long)n * D;
     const bf16* kh = k + bh * (long)m * D;
@@ -108,38 +155,51 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const float* lh = lse2 + bh * (long)n_pad;
     const float* dh = Dw + bh * (long)n_pad;
 
-    // This lane's key row: B operand of S = Q K^T and of dP = dO V^T.
-    bf16x8 kreg[D / 16], vreg[DV / 16];
+    // K rows j0 .. j0+255 into LDS (rows past m read as zeros: their S and
+    // P only reach dK and dV rows that are never written).
+    {
+        TileLoader<D, C::BN, NW> ldK;
+        ldK.init(wave, lane);
+        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)m * D * 2), j0, wave);
+    }
+    // This lane's V row for key tile kt (key kw0 + 32 kt + li): B operand of
+    // dP = dO V^T.
+    bf16x8 vreg[2][DV / 16];
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-        kreg[kc] = myk < m ? gload_bf16x8(kh + (long)myk * D + 16 * kc + 8 * g) : bf16x8{};
+    for (int kt = 0; kt < 2; ++kt) {
+        const int key = kw0 + 32 * kt + li;
 #pragma unroll
-    for (int kc = 0; kc < DV / 16; ++kc)
-        vreg[kc] = myk < m ? gload_bf16x8(vh + (long)myk * DV + 16 * kc + 8 * g) : bf16x8{};
+        for (int kc = 0; kc < DV / 16; ++kc)
+            vreg[kt][kc] = key < m ? gload_bf16x8(vh + (long)key * DV + 16 * kc + 8 * g) : bf16x8{};
+    }
 
     TileOffsets<D> toQ;
     toQ.init(lane);
     TileOffsets<DV> toO;
     toO.init(lane);
+    const bf16* Kw = sK + C::KW * wave * D;  // this wave's 64 K rows
 
-    const int i_begin = CAUSAL ? (j0 / BM) * BM : 0;
+    const int i_begin = CAUSAL ? j0 : 0;
     const int i_end = (n + BM - 1) / BM * BM;
-    const int nsteps = (i_end - i_begin) / BM;
+    const int nsteps = i_end > i_begin ? (i_end - i_begin) / BM : 0;
+    // Causal: the query tiles below the workgroup's last key straddle the
+    // diagonal and are masked; the rest see every key of the workgroup.
+    const int n_masked = CAUSAL ? min(nsteps, C::BN / BM) : 0;
 
-    // Stage query tile i0 into a buffer: Q and dO rows (rows past n come
-    // back as zeros; their LSE2 is +inf, so P = 0 and they contribute
-    // nothing), and the per-row LSE2 and D.
+    // Query tile i0 into a buffer: Q and dO rows (rows past n come back as
+    // zeros; their LSE2 is +inf, so P = 0 and they contribute nothing), and
+    // the per-row LSE2 and D.
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)n * D * 2);
     const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)n * DV * 2);
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(lh, (uint32_t)n_pad * 4);
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(dh, (uint32_t)n_pad * 4);
-    TileLoader<D, BM, 4> ldQ;
+    TileLoader<D, BM, NW> ldQ;
     ldQ.init(wave, lane);
-    TileLoader<DV, BM, 4> ldO;
+    TileLoader<DV, BM, NW> ldO;
     ldO.init(wave, lane);
     auto stage = [&](auto buf_, int i0) __attribute__((always_inline)) {
-        tile_fill<D, BM, 4>(ldQ, pick(buf_, sQ0, sQ1), rQ, i0, wave);
-        tile_fill<DV, BM, 4>(ldO, pick(buf_, sO0, sO1), rO, i0, wave);
+        tile_fill<D, BM, NW>(ldQ, pick(buf_, sQ0, sQ1), rQ, i0, wave);
+        tile_fill<DV, BM, NW>(ldO, pick(buf_, sO0, sO1), rO, i0, wave);
         if (wave == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (ATTN_LDS void*)pick(buf_, sL0, sL1), 4,
                                                      4 * lane, 4 * i0, 0, 0);
@@ -148,126 +208,124 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                                                      4 * lane, 4 * i0, 0, 0);
     };
 
-    f32x16 accK[D / 32], accV[DV / 32];
+    f32x16 accK[2][D / 32], accV[2][DV / 32];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) accK[t] = zero16();
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-    for (int t = 0; t < DV / 32; ++t) accV[t] = zero16();
+        for (int x = 0; x < D / 32; ++x) accK[kt][x] = zero16();
+#pragma unroll
+        for (int x = 0; x < DV / 32; ++x) accV[kt][x] = zero16();
+    }
 
-    // One query tile.  The step is a fixed sequence of NA + NC products,
-    // issued one per slot in this order:
-    //   A ops (per query half t): S[t] += Q_t K^T (D/16), dP[t] += dO_t V^T (DV/16)
-    //   C ops (per t, c):         dV += P^T dO (DV/32), dK += dS^T Q (D/32)
-    // Each product's LDS operand is fetched PD slots ahead, and the softmax
-    // of one half is spread over the slots of the other half's products, so
-    // that the matrix cores, the LDS and the vector ALUs work at the same
-    // time.  Slots are fenced with sched_barrier so the compiler keeps this
-    // order.  MASKED steps apply the causal mask (tiles on the diagonal).
+    // One query tile: the SC schedule, one MFMA per slot, fenced with
+    // sched_barrier so that the operand reads (LA slots ahead), the matrix
+    // products and the softmax work interleave as written.  MASKED steps
+    // apply the causal mask.
     auto compute = [&](auto buf_, auto masked_, int i0) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_)::value;
         const bf16* Qs = pick(buf_, sQ0, sQ1);
         const bf16* Os = pick(buf_, sO0, sO1);
         const float* Ls = pick(buf_, sL0, sL1);
-        const float* Dsm = pick(buf_, sD0, sD1);
+        const float* Ds = pick(buf_, sD0, sD1);
 
-        constexpr int KA = D / 16, KB = DV / 16;
-        constexpr int NAT = KA + KB, NA = 2 * NAT;
-        constexpr int NCX = DV / 32 + D / 32;
-        constexpr int NCT = 2 * NCX, NC = 2 * NCT;
-        constexpr int NOPS = NA + NC;
-        constexpr int PD = 4;
-
-        auto load_op = [&](auto oc_) __attribute__((always_inline)) -> bf16x8 {
-            constexpr int o = decltype(oc_)::value;
-            if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
-                if constexpr (r < KA) return tile_read8_at<D>(Qs, toQ, 32 * t, r);
-                else return tile_read8_at<DV>(Os, toO, 32 * t, r - KA);
+        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
+            constexpr int f = decltype(f_)::value;
+            if constexpr (f < SC::F_K) {
+                return tile_read8_at<D>(Qs, toQ, 0, f);
+            } else if constexpr (f < SC::F_DO) {
+                constexpr int kt = (f - SC::F_K) / SC::KA, r = (f - SC::F_K) % SC::KA;
+                return tile_read8_at<D>(Kw, toQ, 32 * kt, r);
+            } else if constexpr (f < SC::F_DOT) {
+                return tile_read8_at<DV>(Os, toO, 0, f - SC::F_DO);
+            } else if constexpr (f < SC::F_QT) {
+                constexpr int c = (f - SC::F_DOT) / SC::NXV, x = (f - SC::F_DOT) % SC::NXV;
+                return tile_read_tr_at<DV>(Os, toO, 16 * c, x);
             } else {
-                constexpr int oc = o - NA;
-                constexpr int t = oc / NCT, rc = oc % NCT;
-                constexpr int c = rc / NCX, x = rc % NCX;
-                if constexpr (x < DV / 32) return tile_read_tr_at<DV>(Os, toO, 32 * t + 16 * c, x);
-                else return tile_read_tr_at<D>(Qs, toQ, 32 * t + 16 * c, x - DV / 32);
+                constexpr int c = (f - SC::F_QT) / SC::NX, x = (f - SC::F_QT) % SC::NX;
+                return tile_read_tr_at<D>(Qs, toQ, 16 * c, x);
             }
         };
 
-        f32x16 S[2], dP[2];
+        f32x16 S[2], dP[2];          // S is overwritten by P
         bf16x8 Pb[2][2], dSb[2][2];
         f32x4 l4[4], d4[4];
-        float p[16], ds[16];
+        bf16x8 fr[SC::NF];
 
-        // key > query  <=>  32t + 8vq + r < myk - i0 - 4g
-        const int mask_lim = myk - i0 - 4 * g;
-        auto load_stats = [&](auto t_, auto vq_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, vq = decltype(vq_)::value;
-            l4[vq] = *reinterpret_cast<const f32x4*>(Ls + 32 * t + 8 * vq + 4 * g);
-            d4[vq] = *reinterpret_cast<const f32x4*>(Dsm + 32 * t + 8 * vq + 4 * g);
+        // Query of accumulator slot e: i0 + 8(e>>2) + 4g + (e&3); key of
+        // tile kt: kw0 + 32kt + li.  The slot is masked when key > query,
+        // i.e. when 8(e>>2) + (e&3) < lim[kt].
+        int lim[2];
+        if constexpr (MASKED) {
+            lim[0] = kw0 + li - i0 - 4 * g;
+            lim[1] = lim[0] + 32;
+        }
+
+        auto p_elem = [&](auto i_) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_)::value;
+            constexpr int kt = SC::elem_kt(i), e = SC::elem_e(i), vq = e >> 2, r = e & 3;
+            float pv = fast_exp2(__builtin_fmaf(S[kt][e], c2, -l4[vq][r]));
+            if constexpr (MASKED) pv = (8 * vq + r < lim[kt]) ? 0.f : pv;
+            S[kt][e] = pv;
+            if constexpr (i % 8 == 7) {
+                constexpr int c = SC::elem_c(i), b = 8 * c;
+                Pb[kt][c] = pack8(S[kt][b], S[kt][b + 1], S[kt][b + 2], S[kt][b + 3], S[kt][b + 4],
+                                  S[kt][b + 5], S[kt][b + 6], S[kt][b + 7]);
+            }
         };
-        // One accumulator slot E of half T: P = exp2(S*scale*log2e - LSE2),
-        // dS = P (dP - D); after slots 7 and 15 the eight values are rounded
-        // to bf16 as one operand.
-        auto softmax_elem = [&](auto t_, auto e_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, e = decltype(e_)::value;
-            constexpr int vq = e >> 2, r = e & 3;
-            float pv = fast_exp2(__builtin_fmaf(S[t][e], c2, -l4[vq][r]));
-            if constexpr (MASKED) pv = (32 * t + 8 * vq + r < mask_lim) ? 0.f : pv;
-            p[e] = pv;
-            ds[e] = pv * (dP[t][e] - d4[vq][r]);
-            if constexpr ((e & 7) == 7) {
-                constexpr int c = e >> 3, b = 8 * c;
-                Pb[t][c] = pack8(p[b], p[b + 1], p[b + 2], p[b + 3], p[b + 4], p[b + 5], p[b + 6], p[b + 7]);
-                dSb[t][c] = pack8(ds[b], ds[b + 1], ds[b + 2], ds[b + 3], ds[b + 4], ds[b + 5],
-                                  ds[b + 6], ds[b + 7]);
+        auto ds_elem = [&](auto i_) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_)::value;
+            constexpr int kt = SC::elem_kt(i), e = SC::elem_e(i), vq = e >> 2, r = e & 3;
+            dP[kt][e] = S[kt][e] * (dP[kt][e] - d4[vq][r]);
+            if constexpr (i % 8 == 7) {
+                constexpr int c = SC::elem_c(i), b = 8 * c;
+                dSb[kt][c] = pack8(dP[kt][b], dP[kt][b + 1], dP[kt][b + 2], dP[kt][b + 3],
+                                   dP[kt][b + 4], dP[kt][b + 5], dP[kt][b + 6], dP[kt][b + 7]);
             }
         };
 
-        // The softmax of each half is spread one or two accumulator slots per
-        // product over a window of slots, so that its exponentials and
-        // conversions overlap the matrix products instead of stalling them:
-        // half 0 over the A ops of half 1, half 1 over the C ops of half 0
-        // (finishing each bf16 operand before the first product that reads it).
-        constexpr int W0[2] = {NAT + 2, NA + 2};
-        constexpr int W1[2] = {NA, NA + NCT + NCX - 1};
-        static_assert(W1[0] > W0[0] && W1[1] > W0[1], "softmax windows");
-        static_assert(W0[1] + (7 * (W1[1] - W0[1])) / 16 < NA + NCT, "half 1 low operand in time");
-
-        bf16x8 fr[PD];
-        static_for<PD>([&](auto o_) { fr[decltype(o_)::value] = load_op(o_); });
+        static_for<SC::NF>([&](auto f_) {
+            constexpr int f = decltype(f_)::value;
+            if constexpr (SC::issue_at(f, LA) == 0) fr[f] = load_frag(f_);
+        });
         __builtin_amdgcn_sched_barrier(0);
 
-        static_for<NOPS>([&](auto o_) {
-            constexpr int o = decltype(o_)::value;
-            const bf16x8 cur = fr[o % PD];
-            if constexpr (o + PD < NOPS)
-                fr[o % PD] = load_op(std::integral_constant<int, o + PD>{});
-            if constexpr (o < NA) {
-                constexpr int t = o / NAT, r = a_order<KA, KB>(o % NAT);
-                if constexpr (o % NAT == 0) {
-                    S[t] = zero16();
-                    dP[t] = zero16();
-                }
-                if constexpr (r < KA) S[t] = mfma32(cur, kreg[r], S[t]);
-                else dP[t] = mfma32(cur, vreg[r - KA], dP[t]);
+        static_for<SC::NJ>([&](auto j_) {
+            constexpr int j = decltype(j_)::value;
+            // operand reads for later slots
+            static_for<SC::NF>([&](auto f_) {
+                constexpr int f = decltype(f_)::value;
+                if constexpr (j > 0 && SC::issue_at(f, LA) == j) fr[f] = load_frag(f_);
+            });
+            // statistics
+            static_for<4>([&](auto vq_) {
+                constexpr int vq = decltype(vq_)::value;
+                if constexpr (SC::l_slot(vq) == j)
+                    l4[vq] = *reinterpret_cast<const f32x4*>(Ls + 8 * vq + 4 * g);
+                if constexpr (SC::d_slot(vq) == j)
+                    d4[vq] = *reinterpret_cast<const f32x4*>(Ds + 8 * vq + 4 * g);
+            });
+            // the product of this slot
+            constexpr int kt = j % 2;
+            if constexpr (j < SC::J_DP) {
+                constexpr int r = j / 2;
+                if constexpr (r == 0) S[kt] = zero16();
+                S[kt] = mfma32(fr[r], fr[SC::F_K + kt * SC::KA + r], S[kt]);
+            } else if constexpr (j < SC::J_DV) {
+                constexpr int r = (j - SC::J_DP) / 2;
+                if constexpr (r == 0) dP[kt] = zero16();
+                dP[kt] = mfma32(fr[SC::F_DO + r], vreg[kt][r], dP[kt]);
+            } else if constexpr (j < SC::J_DK) {
+                constexpr int cx = (j - SC::J_DV) / 2, c = cx / SC::NXV, x = cx % SC::NXV;
+                mfma32_agpr(Pb[kt][c], fr[SC::F_DOT + cx], accV[kt][x]);
             } else {
-                constexpr int oc = o - NA;
-                constexpr int t = oc / NCT, rc = oc % NCT;
-                constexpr int c = rc / NCX, x = rc % NCX;
-                if constexpr (x < DV / 32) accV[x] = mfma32(Pb[t][c], cur, accV[x]);
-                else accK[x - DV / 32] = mfma32(dSb[t][c], cur, accK[x - DV / 32]);
+                constexpr int cx = (j - SC::J_DK) / 2, c = cx / SC::NX, x = cx % SC::NX;
+                mfma32_agpr(dSb[kt][c], fr[SC::F_QT + cx], accK[kt][x]);
             }
-            static_for<2>([&](auto t_) {
-                constexpr int t = decltype(t_)::value;
-                constexpr int L = W1[t] - W0[t];
-                // statistics for row group vq one slot before its first element
-                static_for<4>([&](auto vq_) {
-                    constexpr int vq = decltype(vq_)::value;
-                    if constexpr (W0[t] + (4 * vq * L) / 16 - 1 == o) load_stats(t_, vq_);
-                });
-                static_for<16>([&](auto e_) {
-                    constexpr int e = decltype(e_)::value;
-                    if constexpr (W0[t] + (e * L) / 16 == o) softmax_elem(t_, e_);
-                });
+            // softmax work of this slot
+            static_for<32>([&](auto i_) {
+                constexpr int i = decltype(i_)::value;
+                if constexpr (SC::p_slot(i) == j) p_elem(i_);
+                if constexpr (SC::ds_slot(i) == j) ds_elem(i_);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -291,34 +349,41 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // Step s uses buffer s & 1; the masked run has an even length unless it
+    // covers every step, so the plain loop starts on buffer 0.
     int s = 0;
-    if constexpr (CAUSAL) {
-        // Query tiles that overlap keys j0..j0+BN-1 straddle the diagonal;
-        // with BN = 2 BM these are the first two, buffers 0 and 1.
-        static_assert(C::BN == 2 * BM, "two masked steps per key block");
-        if (s < nsteps) do_step(B0{}, MaskOn{}, s++);
-        if (s < nsteps) do_step(B1{}, MaskOn{}, s++);
+    for (; s + 1 < n_masked; s += 2) {
+        do_step(B0{}, MaskOn{}, s);
+        do_step(B1{}, MaskOn{}, s + 1);
     }
+    if (s < n_masked) do_step(B0{}, MaskOn{}, s++);
     for (; s + 1 < nsteps; s += 2) {
         do_step(B0{}, MaskOff{}, s);
         do_step(B1{}, MaskOff{}, s + 1);
     }
     if (s < nsteps) do_step(B0{}, MaskOff{}, s);
 
-    // Accumulator slot vv of tile nt holds key kw0 + 8*(vv>>2) + 4g + (vv&3),
-    // column 32*nt + li.
+    // wait states between the last MFMA writing an accumulator and the
+    // reads below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // Accumulator slot vv of tile (kt, x) holds key kw0 + 32kt + 8(vv>>2) +
+    // 4g + (vv&3), column 32x + li.
     bf16* dkh = dk + bh * (long)m * D;
     bf16* dvh = dvo + bh * (long)m * DV;
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) {
-        const int key = kw0 + 8 * (vv >> 2) + 4 * g + (vv & 3);
-        if (key < m) {
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-            for (int nt = 0; nt < D / 32; ++nt)
-                dkh[(long)key * D + 32 * nt + li] = (bf16)(accK[nt][vv] * scale);
+        for (int vv = 0; vv < 16; ++vv) {
+            const int key = kw0 + 32 * kt + 8 * (vv >> 2) + 4 * g + (vv & 3);
+            if (key < m) {
 #pragma unroll
-            for (int nt = 0; nt < DV / 32; ++nt)
-                dvh[(long)key * DV + 32 * nt + li] = (bf16)accV[nt][vv];
+                for (int x = 0; x < D / 32; ++x)
+                    dkh[(long)key * D + 32 * x + li] = (bf16)(accK[kt][x][vv] * scale);
+#pragma unroll
+                for (int x = 0; x < DV / 32; ++x)
+                    dvh[(long)key * DV + 32 * x + li] = (bf16)accV[kt][x][vv];
+            }
         }
     }
 }

@@ -52,6 +52,17 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product with the accumulator pinned in AGPRs, for kernels whose
+// accumulators do not fit next to their other operands in the 256 VGPRs.
+// Written out because the compiler places all MFMA results in one register
+// file.  The compiler does not see this as an MFMA, so the hazards it
+// would cover are covered here: s_nop 1 gives the two wait states an MFMA
+// needs after a VALU write of its A or B operand; the accumulator is only
+// ever touched by this chain, and callers wait (s_nop) before reading it.
+__device__ __forceinline__ void mfma32_agpr(bf16x8 a, bf16x8 b, f32x16& acc) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
