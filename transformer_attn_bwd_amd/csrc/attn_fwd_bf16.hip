@@ -1,13 +1,23 @@
 // Forward attention on bf16 MFMA with float32 softmax statistics; emits O
-// and the per-row log-sum-exp that the backward uses to recompute P.
+// and the per-row log-sum-exp that the backward uses to recompute P
+// (mlgrind "Forward"; "Attention Backpropagation: Step by step
+// derivation", section Forward Pass).
 //
-// Per workgroup: 128 query rows of one (batch, head), 32 per wave.  Each
-// step stages 64 keys: K row-major and V transposed in LDS (double
-// buffered, next tile prefetched into registers during the current one).
-// The wave computes S^T = K Q^T so that a lane owns one query: the online
-// row max and row sum are per-lane values (plus one exchange with the lane
-// 32 away), and P^T in accumulator layout feeds O^T += V^T P^T directly as
-// the B operand (row-of-C order), with no trip through LDS.
+// Layout: one workgroup per 256 queries of a head, four waves, each wave
+// owning two 32-query MFMA tiles.  The lane owns a query column of the
+// transposed products
+//     S^T = K Q^T,   O^T += V^T P^T,
+// so this lane's row of Q is a register-resident B operand, the online
+// row max and row sum are per-lane values (plus one exchange with the
+// lane 32 away, which holds the other half of the keys), and P^T in
+// accumulator layout is the B operand of the O product in row-of-C order
+// (see attn_device.h).  Every 32-key tile of K and V is staged once in LDS
+// and each fragment read from it feeds two MFMAs, one per query tile.
+//
+// The running max is raised lazily: the accumulators and the row sum are
+// rescaled only when some row's max grows by more than 2^8 (in the base-2
+// domain), so P = exp2(S * scale * log2e - m) stays below 2^8 and the
+// rescale, which touches every accumulator, is rare.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -16,192 +26,268 @@ namespace {
 
 template <int D, int DV>
 struct FwdCfg {
-    static constexpr int BM = 128;          // queries per workgroup
-    static constexpr int BN = 64;           // keys per step
-    static constexpr int LDK = D + 8;       // row stride of K in LDS (elements)
-    static constexpr int LDT = BN + 4;      // row stride of V^T in LDS
-    static constexpr int K_ITEMS = BN * D / 8;            // 16-byte chunks of K
-    static constexpr int VT_ITEMS = (BN / 4) * (DV / 8);  // 4x8 blocks of V
-    static constexpr int K_PER_T = (K_ITEMS + 255) / 256;
-    static constexpr int VT_PER_T = (VT_ITEMS + 255) / 256;
+    static constexpr int NW = 4;              // waves per workgroup
+    static constexpr int BM = 2 * 32 * NW;    // queries per workgroup
+    static constexpr int BN = 32;             // keys per step
+    static constexpr int PD = 4;              // operand reads issued ahead
 };
 
+constexpr float kRescaleThreshold = 8.f;     // log2 of the largest P allowed
+
 template <int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int n, int m, float c2) {
     using C = FwdCfg<D, DV>;
-    __shared__ __align__(16) bf16 sK[2][C::BN * C::LDK];
-    __shared__ __align__(16) bf16 sVT[2][DV * C::LDT];
+    constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
+    constexpr int KA = D / 16, NXV = DV / 32;
+    // One LDS variable per buffer: reads of one buffer are then known not
+    // to alias the asynchronous fills of the other.
+    __shared__ __align__(1024) bf16 sK0[BN * D];
+    __shared__ __align__(1024) bf16 sK1[BN * D];
+    __shared__ __align__(1024) bf16 sV0[BN * DV];
+    __shared__ __align__(1024) bf16 sV1[BN * DV];
+    auto pick = [](auto b_, auto* x0, auto* x1) __attribute__((always_inline)) {
+        if constexpr (decltype(b_)::value == 0) return x0;
+        else return x1;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
     const long bh = blockIdx.x;
     const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
     const int i0 = qb * C::BM;
-    const int myq = i0 + wave * 32 + li;
 
     const bf16* qh = q + bh * (long)n * D;
     const bf16* kh = k + bh * (long)m * D;
     const bf16* vh = v + bh * (long)m * DV;
 
-    // This lane's query row as the B operand of S^T = K Q^T (natural k order).
-    bf16x8 qreg[D / 16];
+    // A negative scale is handled by negating Q, so that the row max of
+    // S * c2 is c2 times the row max of the computed S.
+    const bool neg = c2 < 0.f;
+    const float cs = neg ? -c2 : c2;
+
+    // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31), one
+    // tile from each half of the workgroup's rows (even causal work).
+    int myq[2];
+    bf16x8 qreg[2][KA];
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-        if (myq < n) qreg[kc] = gload_bf16x8(qh + (long)myq * D + 16 * kc + 8 * g);
-        else qreg[kc] = bf16x8{};
+    for (int t = 0; t < 2; ++t) {
+        myq[t] = i0 + (C::BM / 2) * t + 32 * wave + li;
+        const bool ok = myq[t] < n;
+#pragma unroll
+        for (int kc = 0; kc < KA; ++kc) {
+            bf16x8 x = ok ? gload_bf16x8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : bf16x8{};
+            if (neg) x = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
+            qreg[t][kc] = x;
+        }
     }
+
+    TileOffsets<D> toK;
+    toK.init(lane);
+    TileOffsets<DV> toV;
+    toV.init(lane);
 
     const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
-    const int nsteps = (k_end + C::BN - 1) / C::BN;
+    const int nsteps = (k_end + BN - 1) / BN;
+    int n_plain = min(nsteps, m / BN);
+    if (CAUSAL) n_plain = min(n_plain, i0 / BN);
 
-    u32x4 kst[C::K_PER_T];
-    u32x4 vst[C::VT_PER_T][4];
+    // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead;
+    // rows past m come back as zeros and are masked.
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)m * D * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)m * DV * 2);
+    TileLoader<D, BN, NW> ldK;
+    ldK.init(wave, lane);
+    TileLoader<DV, BN, NW> ldV;
+    ldV.init(wave, lane);
+    auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
+        tile_fill<D, BN, NW>(ldK, pick(buf_, sK0, sK1), rK, k0, wave);
+        tile_fill<DV, BN, NW>(ldV, pick(buf_, sV0, sV1), rV, k0, wave);
+    };
 
-    auto fetch = [&](int k0) {
+    // O^T accumulators (AGPRs), running max (base 2) and this lane's part
+    // of the running sum, per query tile.
+    f32x16 acc[NXV][2];
 #pragma unroll
-        for (int it = 0; it < C::K_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::K_ITEMS) {
-                const int r = e / (D / 8), cg = e % (D / 8);
-                const int key = k0 + r;
-                kst[it] = key < m ? gload16(kh + (long)key * D + 8 * cg) : u32x4{0, 0, 0, 0};
+    for (int x = 0; x < NXV; ++x) {
+        acc[x][0] = zero16();
+        acc[x][1] = zero16();
+    }
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+
+    // One key tile: fragments f < KA are K rows (S^T[t] += K Q_t^T, two
+    // MFMAs each); then the softmax; then fragments (c, x) of V^T for
+    // O^T[x][t] += V^T P^T[t], two MFMAs each.  The exponentials of key
+    // half 1 run during the half-0 products.
+    auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_)::value;
+        const bf16* Ks = pick(buf_, sK0, sK1);
+        const bf16* Vs = pick(buf_, sV0, sV1);
+        constexpr int NF = KA + 2 * NXV;
+
+        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
+            constexpr int f = decltype(f_)::value;
+            if constexpr (f < KA) {
+                return tile_read8_at<D>(Ks, toK, 0, f);
+            } else {
+                constexpr int cx = f - KA, c = cx / NXV, x = cx % NXV;
+                return tile_read_tr_at<DV>(Vs, toV, 16 * c, x);
+            }
+        };
+
+        f32x16 S[2];
+        bf16x8 Pb[2][2];
+        float mb[2];
+
+        // Accumulator slot e of tile t holds key k0 + 4g + kr(e), kr(e) =
+        // 8(e>>2) + (e&3); it is visible when kr(e) <= lim[t].  Masked slots
+        // are left out of the max and get P = 0.
+        int lim[2];
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                lim[t] = m - 1 - k0 - 4 * g;
+                if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] - k0 - 4 * g);
             }
         }
+        auto softmax_head = [&]() __attribute__((always_inline)) {
+            float m_new[2];
+            bool grow = false;
 #pragma unroll
-        for (int it = 0; it < C::VT_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::VT_ITEMS) {
-                const int rg = e / (DV / 8), cg = e % (DV / 8);
+            for (int t = 0; t < 2; ++t) {
+                float mx = -INFINITY;
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int key = k0 + 4 * rg + x;
-                    vst[it][x] = key < m ? gload16(vh + (long)key * DV + 8 * cg)
-                                         : u32x4{0, 0, 0, 0};
+                for (int e = 0; e < 16; ++e) {
+                    if constexpr (MASKED)
+                        mx = (8 * (e >> 2) + (e & 3) > lim[t]) ? mx : fmaxf(mx, S[t][e]);
+                    else
+                        mx = fmaxf(mx, S[t][e]);
+                }
+                mx = fmaxf(mx, xor_lane32(mx));
+                m_new[t] = mx == -INFINITY ? m_run[t] : fmaxf(m_run[t], mx * cs);
+                grow |= m_new[t] > m_run[t] + kRescaleThreshold;
+            }
+            if (__any(grow)) {
+                // wait states after the last MFMA that wrote the accumulators
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float alpha = m_new[t] == m_run[t] ? 1.f : fast_exp2(m_run[t] - m_new[t]);
+                    l_run[t] *= alpha;
+#pragma unroll
+                    for (int x = 0; x < NXV; ++x) acc[x][t] *= alpha;
+                    m_run[t] = m_new[t];
                 }
             }
-        }
-    };
-    auto commit = [&](int buf) {
 #pragma unroll
-        for (int it = 0; it < C::K_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::K_ITEMS) {
-                const int r = e / (D / 8), cg = e % (D / 8);
-                lds_write16(&sK[buf][r * C::LDK + 8 * cg], kst[it]);
+            for (int t = 0; t < 2; ++t) mb[t] = m_run[t] == -INFINITY ? 0.f : m_run[t];
+        };
+        auto p_half = [&](auto t_, auto c_) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_)::value, c = decltype(c_)::value;
+            float p8[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                constexpr int e = 8 * c;
+                float pv = fast_exp2(__builtin_fmaf(S[t][e + s], cs, -mb[t]));
+                if constexpr (MASKED) pv = (8 * ((e + s) >> 2) + ((e + s) & 3) > lim[t]) ? 0.f : pv;
+                p8[s] = pv;
+                l_run[t] += pv;
             }
-        }
-#pragma unroll
-        for (int it = 0; it < C::VT_PER_T; ++it) {
-            const int e = tid + it * 256;
-            if (e < C::VT_ITEMS) {
-                const int rg = e / (DV / 8), cg = e % (DV / 8);
-#pragma unroll
-                for (int y = 0; y < 8; ++y)
-                    lds_write8(&sVT[buf][(8 * cg + y) * C::LDT + 4 * rg], column4(vst[it], y));
+            Pb[t][c] = pack8(p8[0], p8[1], p8[2], p8[3], p8[4], p8[5], p8[6], p8[7]);
+        };
+
+        bf16x8 fr[PD];
+        static_for<PD>([&](auto f_) { fr[decltype(f_)::value] = load_frag(f_); });
+        __builtin_amdgcn_sched_barrier(0);
+
+        static_for<NF>([&](auto f_) {
+            constexpr int f = decltype(f_)::value;
+            const bf16x8 cur = fr[f % PD];
+            if constexpr (f + PD < NF) fr[f % PD] = load_frag(std::integral_constant<int, f + PD>{});
+            if constexpr (f < KA) {
+                static_for<2>([&](auto t_) {
+                    constexpr int t = decltype(t_)::value;
+                    if constexpr (f == 0) S[t] = zero16();
+                    S[t] = mfma32(cur, qreg[t][f], S[t]);
+                });
+                if constexpr (f == KA - 1) {
+                    softmax_head();
+                    p_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+                    p_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+                }
+            } else {
+                constexpr int cx = f - KA, c = cx / NXV, x = cx % NXV;
+                static_for<2>([&](auto t_) {
+                    constexpr int t = decltype(t_)::value;
+                    mfma32_agpr(cur, Pb[t][c], acc[x][t]);
+                });
+                if constexpr (c == 0 && x == 0)
+                    p_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+                if constexpr (c == 0 && x == (NXV > 1 ? 1 : 0))
+                    p_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
             }
-        }
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
 
-    f32x16 acc[DV / 32];
-#pragma unroll
-    for (int mt = 0; mt < DV / 32; ++mt) acc[mt] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using MaskOn = std::integral_constant<bool, true>;
+    using MaskOff = std::integral_constant<bool, false>;
 
-    if (nsteps > 0) {
-        fetch(0);
-        commit(0);
-    }
+    auto do_step = [&](auto buf_, auto masked_, int s) __attribute__((always_inline)) {
+        constexpr int buf = decltype(buf_)::value;
+        const int k0 = s * BN;
+        if (s + 1 < nsteps) stage(std::integral_constant<int, buf ^ 1>{}, k0 + BN);
+        compute(buf_, masked_, k0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    if (nsteps > 0) stage(B0{}, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int step = 0; step < nsteps; ++step) {
-        const int buf = step & 1;
-        const int k0 = step * C::BN;
-        const bool has_next = step + 1 < nsteps;
-        if (has_next) fetch(k0 + C::BN);
-
-        const bf16* Ks = sK[buf];
-        const bf16* VTs = sVT[buf];
-        f32x16 S[2];
-        S[0] = zero16();
-        S[1] = zero16();
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 a = lds_read8(Ks + (32 * t + li) * C::LDK + 16 * kc + 8 * g);
-                S[t] = mfma32(a, qreg[kc], S[t]);
-            }
-        }
-
-        const bool need_mask = (CAUSAL && k0 + C::BN - 1 > i0) || (k0 + C::BN > m);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                float sv = S[t][vv] * c2;
-                if (need_mask) {
-                    const int key = k0 + 32 * t + 8 * (vv >> 2) + 4 * g + (vv & 3);
-                    if (key >= m || (CAUSAL && key > myq)) sv = -INFINITY;
-                }
-                S[t][vv] = sv;
-                mx = fmaxf(mx, sv);
-            }
-        }
-        mx = fmaxf(mx, xor_lane32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float base = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - base);
-        float psum = 0.f;
-        bf16x8 Pb[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            float p[16];
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                p[vv] = fast_exp2(S[t][vv] - base);
-                psum += p[vv];
-            }
-            Pb[t][0] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            Pb[t][1] = pack8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int mt = 0; mt < DV / 32; ++mt) {
-            acc[mt] = acc[mt] * alpha;
-            const bf16* row = VTs + (32 * mt + li) * C::LDT;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    bf16x8 a = read_rowc_pair(row, 32 * t + 16 * c, g);
-                    acc[mt] = mfma32(a, Pb[t][c], acc[mt]);
-                }
-            }
-        }
-
-        if (has_next) commit(buf ^ 1);
-        __syncthreads();
+    // Both loops start on buffer 0: an odd plain step joins the masked ones.
+    const int n_plain2 = n_plain & ~1;
+    int s = 0;
+    for (; s < n_plain2; s += 2) {
+        do_step(B0{}, MaskOff{}, s);
+        do_step(B1{}, MaskOff{}, s + 1);
     }
+    for (; s + 1 < nsteps; s += 2) {
+        do_step(B0{}, MaskOn{}, s);
+        do_step(B1{}, MaskOn{}, s + 1);
+    }
+    if (s < nsteps) do_step(B0{}, MaskOn{}, s);
 
-    const float l_tot = l_run + xor_lane32(l_run);
-    const float inv = 1.f / l_tot;
-    if (myq < n) {
-        bf16* orow = o + (bh * (long)n + myq) * DV;
+    // wait states between the last MFMA writing an accumulator and the
+    // reads below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // Accumulator slot vv of tile (x, t) holds column 32x + 8(vv>>2) + 4g +
+    // (vv&3) of query myq[t]; the row sum is split over this lane and the
+    // lane 32 away.
 #pragma unroll
-        for (int mt = 0; mt < DV / 32; ++mt) {
+    for (int t = 0; t < 2; ++t) {
+        const float l_tot = l_run[t] + xor_lane32(l_run[t]);
+        const float inv = 1.f / l_tot;
+        if (myq[t] < n) {
+            bf16* orow = o + (bh * (long)n + myq[t]) * DV;
 #pragma unroll
-            for (int vq = 0; vq < 4; ++vq) {
-                bf16x4 w;
+            for (int x = 0; x < NXV; ++x) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[mt][4 * vq + r] * inv);
-                *reinterpret_cast<bf16x4*>(orow + 32 * mt + 8 * vq + 4 * g) = w;
+                for (int vq = 0; vq < 4; ++vq) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[x][t][4 * vq + r] * inv);
+                    *reinterpret_cast<bf16x4*>(orow + 32 * x + 8 * vq + 4 * g) = w;
+                }
             }
+            if (g == 0) lse[bh * (long)n + myq[t]] = (m_run[t] + log2f(l_tot)) * kLn2;
         }
-        if (g == 0) lse[bh * (long)n + myq] = (m_run + log2f(l_tot)) * kLn2;
     }
 }
 
@@ -212,10 +298,10 @@ void launch(const Problem& p, const void* q, const void* k, const void* v, void*
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
     if (p.causal)
-        fwd_bf16_kernel<D, DV, true><<<grid, 256, 0, s>>>(
+        fwd_bf16_kernel<D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
             (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.n, p.m, c2);
     else
-        fwd_bf16_kernel<D, DV, false><<<grid, 256, 0, s>>>(
+        fwd_bf16_kernel<D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
             (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.n, p.m, c2);
 }
 
