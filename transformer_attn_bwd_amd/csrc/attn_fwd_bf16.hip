@@ -11,7 +11,7 @@
 // row max and row sum are per-lane values (plus one exchange with the
 // lane 32 away, which holds the other half of the keys), and P^T in
 // accumulator layout is the B operand of the O product in row-of-C order
-// (see attn_device.h).  Every 32-key tile of K and V is staged once in LDS
+// (see attn_device.h).  Every 64-key tile of K and V is staged once in LDS
 // and each fragment read from it feeds two MFMAs, one per query tile.
 //
 // The running max is raised lazily: the accumulators and the row sum are
@@ -28,7 +28,7 @@ template <int D, int DV>
 struct FwdCfg {
     static constexpr int NW = 4;              // waves per workgroup
     static constexpr int BM = 2 * 32 * NW;    // queries per workgroup
-    static constexpr int BN = 32;             // keys per step
+    static constexpr int BN = 64;             // keys per step
     static constexpr int PD = 4;              // operand reads issued ahead
 };
 
@@ -80,6 +80,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             bf16x8 x = ok ? gload_bf16x8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : bf16x8{};
             if (neg) x = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
             qreg[t][kc] = x;
+            // keep the Q operands in AGPRs (MFMAs read them from there), so
+            // that the VGPRs hold the four S tiles of a step
+            asm volatile("" : "+a"(qreg[t][kc]));
         }
     }
 
@@ -117,33 +120,32 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
 
-    // One key tile: fragments f < KA are K rows (S^T[t] += K Q_t^T, two
-    // MFMAs each); then the softmax; then fragments (c, x) of V^T for
-    // O^T[x][t] += V^T P^T[t], two MFMAs each.  The exponentials of key
-    // half 1 run during the half-0 products.
+    // One key tile: fragments f < NKH KA are K rows of 32-key half kh
+    // (S^T[kh][t] += K Q_t^T, two MFMAs each); then the softmax; then
+    // fragments (c, x) of V^T for O^T[x][t] += V^T P^T[t] over 16-key chunk
+    // c, two MFMAs each.  The exponentials of chunk c+1 run during the
+    // products of chunk c.
     auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_)::value;
+        constexpr int NKH = BN / 32;                    // 32-key halves per step
+        constexpr int NC = 2 * NKH;                     // 16-key chunks per step
         const bf16* Ks = pick(buf_, sK0, sK1);
         const bf16* Vs = pick(buf_, sV0, sV1);
-        constexpr int NF = KA + 2 * NXV;
+        constexpr int NF = NKH * KA + NC * NXV;
 
         auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
             constexpr int f = decltype(f_)::value;
-            if constexpr (f < KA) {
-                return tile_read8_at<D>(Ks, toK, 0, f);
+            if constexpr (f < NKH * KA) {
+                return tile_read8_at<D>(Ks, toK, 32 * (f / KA), f % KA);
             } else {
-                constexpr int cx = f - KA, c = cx / NXV, x = cx % NXV;
+                constexpr int cx = f - NKH * KA, c = cx / NXV, x = cx % NXV;
                 return tile_read_tr_at<DV>(Vs, toV, 16 * c, x);
             }
         };
 
-        f32x16 S[2];
-        bf16x8 Pb[2][2];
+        f32x16 S[NKH][2];
+        bf16x8 Pb[NC][2];
         float mb[2];
-
-        // Accumulator slot e of tile t holds key k0 + 4g + kr(e), kr(e) =
-        // 8(e>>2) + (e&3); it is visible when kr(e) <= lim[t].  Masked slots
-        // are left out of the max and get P = 0.
         int lim[2];
         if constexpr (MASKED) {
 #pragma unroll
@@ -152,6 +154,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] - k0 - 4 * g);
             }
         }
+        auto visible = [&](int kh, int e, int t) __attribute__((always_inline)) {
+            return 32 * kh + 8 * (e >> 2) + (e & 3) <= lim[t];
+        };
         auto softmax_head = [&]() __attribute__((always_inline)) {
             float m_new[2];
             bool grow = false;
@@ -159,18 +164,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int t = 0; t < 2; ++t) {
                 float mx = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    if constexpr (MASKED)
-                        mx = (8 * (e >> 2) + (e & 3) > lim[t]) ? mx : fmaxf(mx, S[t][e]);
-                    else
-                        mx = fmaxf(mx, S[t][e]);
+                for (int kh = 0; kh < NKH; ++kh) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        if constexpr (MASKED) mx = visible(kh, e, t) ? fmaxf(mx, S[kh][t][e]) : mx;
+                        else mx = fmaxf(mx, S[kh][t][e]);
+                    }
                 }
                 mx = fmaxf(mx, xor_lane32(mx));
                 m_new[t] = mx == -INFINITY ? m_run[t] : fmaxf(m_run[t], mx * cs);
                 grow |= m_new[t] > m_run[t] + kRescaleThreshold;
             }
             if (__any(grow)) {
-                // wait states after the last MFMA that wrote the accumulators
                 asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -184,18 +189,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int t = 0; t < 2; ++t) mb[t] = m_run[t] == -INFINITY ? 0.f : m_run[t];
         };
-        auto p_half = [&](auto t_, auto c_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, c = decltype(c_)::value;
+        auto p_chunk = [&](auto c_, auto t_) __attribute__((always_inline)) {
+            constexpr int c = decltype(c_)::value, t = decltype(t_)::value;
+            constexpr int kh = c / 2, e0 = 8 * (c % 2);
             float p8[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                constexpr int e = 8 * c;
-                float pv = fast_exp2(__builtin_fmaf(S[t][e + s], cs, -mb[t]));
-                if constexpr (MASKED) pv = (8 * ((e + s) >> 2) + ((e + s) & 3) > lim[t]) ? 0.f : pv;
+                float pv = fast_exp2(__builtin_fmaf(S[kh][t][e0 + s], cs, -mb[t]));
+                if constexpr (MASKED) pv = visible(kh, e0 + s, t) ? pv : 0.f;
                 p8[s] = pv;
                 l_run[t] += pv;
             }
-            Pb[t][c] = pack8(p8[0], p8[1], p8[2], p8[3], p8[4], p8[5], p8[6], p8[7]);
+            Pb[c][t] = pack8(p8[0], p8[1], p8[2], p8[3], p8[4], p8[5], p8[6], p8[7]);
         };
 
         bf16x8 fr[PD];
@@ -206,27 +211,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             constexpr int f = decltype(f_)::value;
             const bf16x8 cur = fr[f % PD];
             if constexpr (f + PD < NF) fr[f % PD] = load_frag(std::integral_constant<int, f + PD>{});
-            if constexpr (f < KA) {
+            if constexpr (f < NKH * KA) {
+                constexpr int kh = f / KA, r = f % KA;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    if constexpr (f == 0) S[t] = zero16();
-                    S[t] = mfma32(cur, qreg[t][f], S[t]);
+                    if constexpr (r == 0) S[kh][t] = zero16();
+                    S[kh][t] = mfma32(cur, qreg[t][r], S[kh][t]);
                 });
-                if constexpr (f == KA - 1) {
+                if constexpr (f == NKH * KA - 1) {
                     softmax_head();
-                    p_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-                    p_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+                    p_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+                    p_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
                 }
             } else {
-                constexpr int cx = f - KA, c = cx / NXV, x = cx % NXV;
+                constexpr int cx = f - NKH * KA, c = cx / NXV, x = cx % NXV;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    mfma32_agpr(cur, Pb[t][c], acc[x][t]);
+                    mfma32_agpr(cur, Pb[c][t], acc[x][t]);
                 });
-                if constexpr (c == 0 && x == 0)
-                    p_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-                if constexpr (c == 0 && x == (NXV > 1 ? 1 : 0))
-                    p_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+                // chunk c + 1 while the products of chunk c run
+                if constexpr (c + 1 < NC && x == 0)
+                    p_chunk(std::integral_constant<int, c + 1>{}, std::integral_constant<int, 0>{});
+                if constexpr (c + 1 < NC && x == (NXV > 1 ? 1 : 0))
+                    p_chunk(std::integral_constant<int, c + 1>{}, std::integral_constant<int, 1>{});
             }
             __builtin_amdgcn_sched_barrier(0);
         });
