@@ -57,6 +57,14 @@ BF16_SHAPES = [
     _w("bf16_single_row", 1, 1, 1, 1, 128, 64, "bf16", True, 28),
     _w("bf16_cross_1x500_d128", 1, 1, 1, 500, 128, 128, "bf16", False, 29),
     _w("bf16_stress_x30", 1, 1, 70, 90, 128, 64, "bf16", False, 30, 30.0 ** 0.5),
+    # several 256-row workgroups in each direction, ragged against 256, 64, 32
+    _w("bf16_causal_700_d128", 1, 2, 700, 700, 128, 128, "bf16", True, 31),
+    _w("bf16_cross_600x900_d128_dv64", 1, 1, 600, 900, 128, 64, "bf16", False, 32),
+    _w("bf16_causal_520_d64", 2, 1, 520, 520, 64, 64, "bf16", True, 33),
+    # scale signs the kernels treat specially: negative (the forward negates
+    # Q) and zero (uniform P over the visible keys)
+    _w("bf16_negative_scale", 1, 1, 100, 150, 128, 128, "bf16", False, 34, 1.0, -0.1),
+    _w("bf16_zero_scale_causal", 1, 1, 90, 90, 64, 64, "bf16", True, 35, 1.0, 0.0),
 ]
 
 
