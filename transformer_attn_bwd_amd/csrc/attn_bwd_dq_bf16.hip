@@ -13,9 +13,10 @@
 //     S^T = K Q^T,   dP^T = V dO^T,   dQ^T += K^T dS^T,
 // so this lane's rows of Q and dO are register-resident B operands, and
 // the accumulator layout of dS^T (rows = keys) is the B operand of the dQ
-// product in row-of-C order (see attn_device.h).  Every 32-key tile of K
+// product in row-of-C order (see attn_device.h).  Every 64-key tile of K
 // and V is staged once in LDS and each fragment read from it feeds two
-// MFMAs, one per query tile of the wave.  The causal mask (S_ij = -inf for
+// MFMAs, one per query tile of the wave.  The dQ accumulators live in
+// AGPRs.  The causal mask (S_ij = -inf for
 // j > i, i.e. P_ij = 0, eulerpad P8) is applied only in key tiles that
 // reach past the workgroup's first query.
 #include "attn_device.h"
@@ -28,7 +29,7 @@ template <int D, int DV>
 struct DqCfg {
     static constexpr int NW = 4;              // waves per workgroup
     static constexpr int BM = 2 * 32 * NW;    // queries per workgroup
-    static constexpr int BN = 32;             // keys per step
+    static constexpr int BN = 64;             // keys per step
     static constexpr int PD = 4;              // operand reads issued ahead
 };
 
@@ -84,6 +85,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
             oreg[t][kc] = ok ? gload_bf16x8(oh + (long)myq[t] * DV + 16 * kc + 8 * g) : bf16x8{};
+        // Q and dO rows are only MFMA inputs: keep them in AGPRs, leaving
+        // the VGPRs to the S, dP and dS tiles of a 64-key step
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) asm volatile("" : "+a"(qreg[t][kc]));
+#pragma unroll
+        for (int kc = 0; kc < DV / 16; ++kc) asm volatile("" : "+a"(oreg[t][kc]));
         l2[t] = ok ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
         Dq[t] = ok ? Dw[bh * (long)n_pad + myq[t]] : 0.f;
     }
@@ -121,39 +128,38 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         acc[x][1] = zero16();
     }
 
-    // One key tile as a fixed sequence of operand fragments, each read once
-    // from LDS and used by two MFMAs (query tiles 0 and 1):
-    //   f <  KA:            K rows, d chunk f        -> S^T[t]  += K Q_t^T
-    //   f <  KA + KB:       V rows, dv chunk f - KA  -> dP^T[t] += V dO_t^T
-    //   f <  KA + KB + 2NX: K^T, key half c, d block x -> dQ^T[x][t] += K^T dS^T[t]
+    // One key tile (two 32-key halves kh) as a fixed sequence of operand
+    // fragments, each read once from LDS and used by two MFMAs (query tiles
+    // 0 and 1):
+    //   f < FV:   K rows of half kh, d chunk r    -> S^T[kh][t]  += K Q_t^T
+    //   f < FT:   V rows of half kh, dv chunk r   -> dP^T[kh][t] += V dO_t^T
+    //   f < NF:   K^T, 16-key chunk c, d block x  -> dQ^T[x][t] += K^T dS^T
     // P = exp2(S * scale * log2e - LSE2) is formed during the dP products,
-    // dS = P (dP - D) for key half 0 right after them and for key half 1
-    // during the half-0 dQ products.
+    // dS = P (dP - D) for chunk 0 right after them and for chunk c+1 during
+    // the dQ products of chunk c.
     auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_)::value;
         const bf16* Ks = Kbuf(buf_);
         const bf16* Vs = Vbuf(buf_);
         constexpr int KA = D / 16, KB = DV / 16, NX = D / 32;
-        constexpr int NF = KA + KB + 2 * NX;
+        constexpr int NKH = BN / 32, NC = 2 * NKH;
+        constexpr int FV = NKH * KA, FT = FV + NKH * KB, NF = FT + NC * NX;
 
         auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
             constexpr int f = decltype(f_)::value;
-            if constexpr (f < KA) {
-                return tile_read8_at<D>(Ks, toK, 0, f);
-            } else if constexpr (f < KA + KB) {
-                return tile_read8_at<DV>(Vs, toV, 0, f - KA);
+            if constexpr (f < FV) {
+                return tile_read8_at<D>(Ks, toK, 32 * (f / KA), f % KA);
+            } else if constexpr (f < FT) {
+                return tile_read8_at<DV>(Vs, toV, 32 * ((f - FV) / KB), (f - FV) % KB);
             } else {
-                constexpr int cx = f - KA - KB, c = cx / NX, x = cx % NX;
+                constexpr int cx = f - FT, c = cx / NX, x = cx % NX;
                 return tile_read_tr_at<D>(Ks, toK, 16 * c, x);
             }
         };
 
-        f32x16 S[2], dP[2];
-        bf16x8 dSb[2][2];
+        f32x16 S[NKH][2], dP[NKH][2];
+        bf16x8 dSb[NKH][2][2];
 
-        // P for accumulator slot e of tile t, written over S.  The slot's key
-        // is k0 + 4g + kr(e), kr(e) = 8(e>>2) + (e&3); it is visible when
-        // kr(e) <= lim[t] (key < m and, causal, key <= query).
         int lim[2];
         if constexpr (MASKED) {
 #pragma unroll
@@ -162,19 +168,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] - k0 - 4 * g);
             }
         }
-        auto p_elem = [&](auto t_, auto e_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, e = decltype(e_)::value;
-            float pv = fast_exp2(__builtin_fmaf(S[t][e], c2, -l2[t]));
-            if constexpr (MASKED) pv = (8 * (e >> 2) + (e & 3) > lim[t]) ? 0.f : pv;
-            S[t][e] = pv;
+        // P for slot e of tile (kh, t), written over S; key k0 + 32kh + 4g +
+        // 8(e>>2) + (e&3), visible when 32kh + 8(e>>2) + (e&3) <= lim[t].
+        auto p_elem = [&](auto i_) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_)::value;
+            constexpr int kh = i / 32, t = (i / 16) % 2, e = i % 16;
+            float pv = fast_exp2(__builtin_fmaf(S[kh][t][e], c2, -l2[t]));
+            if constexpr (MASKED) pv = (32 * kh + 8 * (e >> 2) + (e & 3) > lim[t]) ? 0.f : pv;
+            S[kh][t][e] = pv;
         };
-        // dS for key half c of tile t, as one bf16 operand (row-of-C order).
-        auto ds_half = [&](auto t_, auto c_) __attribute__((always_inline)) {
-            constexpr int t = decltype(t_)::value, c = decltype(c_)::value;
+        // dS for 16-key chunk c of query tile t (row-of-C order operand).
+        auto ds_chunk = [&](auto c_, auto t_) __attribute__((always_inline)) {
+            constexpr int c = decltype(c_)::value, t = decltype(t_)::value;
+            constexpr int kh = c / 2, h = c % 2;
             float d8[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) d8[s] = S[t][8 * c + s] * (dP[t][8 * c + s] - Dq[t]);
-            dSb[t][c] = pack8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
+            for (int s = 0; s < 8; ++s)
+                d8[s] = S[kh][t][8 * h + s] * (dP[kh][t][8 * h + s] - Dq[t]);
+            dSb[kh][t][h] = pack8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
         };
 
         bf16x8 fr[PD];
@@ -185,39 +196,40 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             constexpr int f = decltype(f_)::value;
             const bf16x8 cur = fr[f % PD];
             if constexpr (f + PD < NF) fr[f % PD] = load_frag(std::integral_constant<int, f + PD>{});
-            if constexpr (f < KA) {
+            if constexpr (f < FV) {
+                constexpr int kh = f / KA, r = f % KA;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    if constexpr (f == 0) S[t] = zero16();
-                    S[t] = mfma32(cur, qreg[t][f], S[t]);
+                    if constexpr (r == 0) S[kh][t] = zero16();
+                    S[kh][t] = mfma32(cur, qreg[t][r], S[kh][t]);
                 });
-            } else if constexpr (f < KA + KB) {
-                constexpr int r = f - KA;
+            } else if constexpr (f < FT) {
+                constexpr int kh = (f - FV) / KB, r = (f - FV) % KB;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    if constexpr (r == 0) dP[t] = zero16();
-                    dP[t] = mfma32(cur, oreg[t][r], dP[t]);
+                    if constexpr (r == 0) dP[kh][t] = zero16();
+                    dP[kh][t] = mfma32(cur, oreg[t][r], dP[kh][t]);
                 });
-                // 32 exponentials (two tiles x 16 slots) over the KB dP slots
-                static_for<32>([&](auto i_) {
+                // 32 NKH exponentials over the NKH KB dP slots
+                static_for<32 * NKH>([&](auto i_) {
                     constexpr int i = decltype(i_)::value;
-                    if constexpr ((i * KB) / 32 == r)
-                        p_elem(std::integral_constant<int, i / 16>{}, std::integral_constant<int, i % 16>{});
+                    if constexpr ((i * KB) / 32 == f - FV) p_elem(i_);
                 });
-                if constexpr (r == KB - 1) {
-                    ds_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-                    ds_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+                if constexpr (f == FT - 1) {
+                    ds_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+                    ds_chunk(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
                 }
             } else {
-                constexpr int cx = f - KA - KB, c = cx / NX, x = cx % NX;
+                constexpr int cx = f - FT, c = cx / NX, x = cx % NX;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    acc[x][t] = mfma32(cur, dSb[t][c], acc[x][t]);
+                    mfma32_agpr(cur, dSb[c / 2][t][c % 2], acc[x][t]);
                 });
-                if constexpr (c == 0 && x == 0)
-                    ds_half(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-                if constexpr (c == 0 && x == (NX > 1 ? 1 : 0))
-                    ds_half(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+                // dS of chunk c + 1 during the products of chunk c
+                if constexpr (c + 1 < NC && x == 0)
+                    ds_chunk(std::integral_constant<int, c + 1>{}, std::integral_constant<int, 0>{});
+                if constexpr (c + 1 < NC && x == (NX > 1 ? 1 : 0))
+                    ds_chunk(std::integral_constant<int, c + 1>{}, std::integral_constant<int, 1>{});
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -254,6 +266,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     if (s < nsteps) do_step(B0{}, MaskOn{}, s);
 
+    // wait states between the last MFMA writing an accumulator and the
+    // reads below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // Accumulator slot vv of tile (x, t) holds column d = 32x + 8(vv>>2) +
     // 4g + (vv&3) of query myq[t].
 #pragma unroll
