@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_device.h", "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "b1b9fca4b436b2ecfd15eb4520178b6e5679462481a78a95ae4aa043850331da",
-    "bytes": {"bwd_dkdv": 8.78e+08, "bwd_dq": 6.254e+08},
+    "sources_sha256": "81c9fcc9375f87e83b1f130e5f71bb6c83c7ab68fb1fe5d6f1242059d908acf0",
+    "bytes": {"bwd_dkdv": 7.745e+08, "bwd_dq": 6.432e+08},
 }
 
 
