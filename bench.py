@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 # same counters read for a plain 1 GiB device copy (x2.0 and x1.0).  They
 # hold only for the kernel sources they were taken on, identified by hash;
 # after any change to those sources the traffic is reported as null.
-KERNEL_SOURCES = ("attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_device.h", "attn_launch.h")
+KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip", "attn_device.h", "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
     "sources_sha256": "81c9fcc9375f87e83b1f130e5f71bb6c83c7ab68fb1fe5d6f1242059d908acf0",
@@ -219,7 +219,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp16": "f16", "fp32": "f32"}[w.dtype],
         "data": "synthetic (seeded N(0,1) inputs, see transformer_attn_bwd_amd/workloads.py)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "m": w.m, "d": w.d,
                    "dv": w.dv, "causal": w.causal, "seed": w.seed, "scale": w.softmax_scale,
@@ -243,7 +243,7 @@ def main():
         "outputs_finite": ok,
         "wall_s_timed": round(t_wall, 3),
     }
-    if not args.no_cpu_baseline and w.dtype == "bf16":
+    if not args.no_cpu_baseline and w.dtype != "fp32":
         print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inputs_cpu, args.cpu_heads)
     print(json.dumps(result), flush=True)

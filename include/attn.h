@@ -26,8 +26,11 @@
  *    arrays: q [B,H,n,d], k [B,H,m,d], v [B,H,m,dv], o and dout [B,H,n,dv],
  *    dq [B,H,n,d], dk [B,H,m,d], dv_out [B,H,m,dv], lse [B,H,n] (float32).
  *  - dtype ATTN_F32: q, k, v, o, dout, dq, dk, dv_out are float32.
- *    dtype ATTN_BF16: they are bfloat16; arithmetic accumulates in float32.
- *  - Supported (d, dv): ATTN_BF16 {(64,64), (128,128), (128,64)};
+ *    dtype ATTN_BF16: they are bfloat16; ATTN_F16: IEEE binary16.  With
+ *    either 16-bit type the products run on 16-bit matrix instructions
+ *    with float32 accumulation; softmax statistics, LSE and D are float32,
+ *    and P and dS are rounded to the input type before their products.
+ *  - Supported (d, dv): ATTN_BF16 and ATTN_F16 {(64,64), (128,128), (128,64)};
  *    ATTN_F32 any d, dv in 1..128.
  *  - The caller owns every buffer.  The library allocates and frees nothing
  *    and never synchronises: work is enqueued on `stream` (a hipStream_t;
@@ -50,7 +53,7 @@ extern "C" {
 #endif
 
 /* Element type of q, k, v, o, dout, dq, dk, dv_out.  lse is always float32. */
-enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 };
 
 /* Return codes. */
 enum attn_status {

@@ -12,9 +12,11 @@ import transformer_attn_bwd_amd as attn
 from transformer_attn_bwd_amd.workloads import Workload, make_inputs
 
 # Tolerances: bf16 path max|err| / max|ref| <= 2e-2 per output tensor; the
-# fp32 path 1e-5 in the same per-tensor relative form (LSE absolute).
-TOL = {"bf16": 2e-2, "fp32": 1e-5}
-LSE_TOL = {"bf16": 1e-3, "fp32": 1e-5}
+# fp32 path 1e-5 in the same per-tensor relative form (LSE absolute).  The
+# float16 path rounds P, dS and the outputs with a unit roundoff of 2^-11
+# instead of bfloat16's 2^-8, so its bar is the bf16 one scaled by 2^-3.
+TOL = {"bf16": 2e-2, "fp16": 2.5e-3, "fp32": 1e-5}
+LSE_TOL = {"bf16": 1e-3, "fp16": 1e-3, "fp32": 1e-5}
 
 
 def say(msg: str) -> None:

@@ -47,6 +47,9 @@ def test_workspace_size(lib):
     assert attn.bwd_workspace_bytes(1, 1, 0, 5, 64, 64) == 0
     assert attn.bwd_workspace_bytes(0, 4, 100, 5, 64, 64) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 96, 96, B.ATTN_BF16, 0) == 0  # unsupported
+    for code in (B.ATTN_BF16, B.ATTN_F16, B.ATTN_F32):
+        assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, 0) == 2 * 6 * 384 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 64, 128, B.ATTN_F16, 0) == 0  # unsupported
 
 
 NULL = None
@@ -76,6 +79,8 @@ def _bwd(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, causal=0, dtype=B
     (dict(d=96, dv=96), B.ATTN_EUNSUPPORTED),
     (dict(d=64, dv=128), B.ATTN_EUNSUPPORTED),
     (dict(dtype=7), B.ATTN_EUNSUPPORTED),
+    (dict(dtype=B.ATTN_F16, d=96, dv=96), B.ATTN_EUNSUPPORTED),
+    (dict(dtype=B.ATTN_F16, d=64, dv=128), B.ATTN_EUNSUPPORTED),
     (dict(dtype=B.ATTN_F32, d=129), B.ATTN_EUNSUPPORTED),
     (dict(n=(1 << 22) + 1, m=(1 << 22) + 1), B.ATTN_EUNSUPPORTED),
 ])
@@ -93,8 +98,9 @@ def test_null_and_misaligned_pointers(lib):
         p = [FAKE] * 9
         p[i] = NULL
         assert _bwd(lib, ptrs=p) == B.ATTN_EINVAL
-    odd = ctypes.c_void_p((1 << 20) + 2)   # not 16-byte aligned for bf16 rows
+    odd = ctypes.c_void_p((1 << 20) + 2)   # not 16-byte aligned for 16-bit rows
     assert _fwd(lib, ptrs=[odd] + [FAKE] * 4) == B.ATTN_EINVAL
+    assert _fwd(lib, ptrs=[odd] + [FAKE] * 4, dtype=B.ATTN_F16) == B.ATTN_EINVAL
 
 
 def test_workspace_checks(lib):
@@ -124,3 +130,19 @@ def test_binding_requires_gpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.fwd(q, q, q)
+
+
+def test_binding_dtype_codes():
+    import torch
+    assert B._dtype_code(torch.zeros(1, dtype=torch.float16)) == B.ATTN_F16
+    assert B._dtype_code(torch.zeros(1, dtype=torch.bfloat16)) == B.ATTN_BF16
+    assert B._dtype_code(torch.zeros(1, dtype=torch.float32)) == B.ATTN_F32
+    with pytest.raises(TypeError):
+        B._dtype_code(torch.zeros(1, dtype=torch.float64))
+
+
+def test_binding_constants_match_header():
+    text = open(HEADER).read()
+    body = re.search(r"enum attn_dtype \{([^}]*)\}", text).group(1)
+    vals = dict((k.strip(), int(v)) for k, v in (e.split("=") for e in body.split(",")))
+    assert vals == {"ATTN_F32": B.ATTN_F32, "ATTN_BF16": B.ATTN_BF16, "ATTN_F16": B.ATTN_F16}

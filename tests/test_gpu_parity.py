@@ -1,8 +1,8 @@
 """GPU parity: the HIP path against the float64 oracle, element by element,
 on seeded inputs that span several tiles and end in ragged tails.
 
-Bar (per output tensor): bf16 max|err| / max|ref| <= 2e-2; float32 1e-5.
-LSE is compared absolutely (bf16 path 1e-3, float32 1e-5).
+Bar (per output tensor): bf16 max|err| / max|ref| <= 2e-2; float16 2.5e-3;
+float32 1e-5.  LSE is compared absolutely (16-bit paths 1e-3, float32 1e-5).
 """
 import numpy as np
 import pytest
@@ -75,6 +75,47 @@ def test_bf16_shapes(w):
     compare_full(w, run_gpu(w, inputs), oracle_full(w, inputs))
 
 
+FP16_SHAPES = [
+    # the same kernels instantiated for IEEE half: every head-width pair,
+    # ragged tails across several workgroups, both masks, and the scale
+    # signs the forward treats specially
+    _w("f16_causal_700_d128", 1, 2, 700, 700, 128, 128, "fp16", True, 51),
+    _w("f16_cross_600x900_d128_dv64", 1, 1, 600, 900, 128, 64, "fp16", False, 52, 3.0),
+    _w("f16_causal_300_d64", 2, 1, 300, 300, 64, 64, "fp16", True, 53),
+    _w("f16_noncausal_129x333_d64", 1, 3, 129, 333, 64, 64, "fp16", False, 54),
+    _w("f16_single_row", 1, 1, 1, 1, 128, 64, "fp16", True, 55),
+    _w("f16_stress_x30", 1, 1, 70, 90, 128, 64, "fp16", False, 56, 30.0 ** 0.5),
+    _w("f16_negative_scale", 1, 1, 100, 150, 128, 128, "fp16", False, 57, 1.0, -0.1),
+    _w("f16_zero_scale_causal", 1, 1, 90, 90, 64, 64, "fp16", True, 58, 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("w", FP16_SHAPES, ids=lambda w: w.name)
+def test_fp16_shapes(w):
+    say(f"case {w.describe()}")
+    inputs = make_inputs(w)
+    compare_full(w, run_gpu(w, inputs), oracle_full(w, inputs))
+
+
+def test_fp16_and_bf16_agree_on_exact_inputs():
+    """Inputs that both 16-bit types hold exactly (small integers times
+    powers of two) give the two instantiations the same problem; their
+    results differ only by the rounding of P, dS and the outputs."""
+    w = _w("both16", 1, 2, 200, 200, 128, 128, "bf16", True, 59)
+    g = torch.Generator().manual_seed(59)
+    base = [torch.randint(-8, 9, s, generator=g).float() / 8
+            for s in ((1, 2, 200, 128),) * 4]
+    ref = oracle_full(w, base)
+    for dt, name in ((torch.bfloat16, "bf16"), (torch.float16, "fp16")):
+        ins = [t.to(dt) for t in base]
+        assert all(torch.equal(a.float(), b) for a, b in zip(ins, base))
+        out = run_gpu(w.with_(dtype=name), ins)
+        for key in ("o", "dq", "dk", "dv"):
+            e = rel_err(to64(out[key]), ref[key])
+            say(f"  {name} {key} {e:.3e}")
+            assert e <= TOL[name], (name, key, e)
+
+
 @pytest.mark.parametrize("w", [BF16_SHAPES[0], BF16_SHAPES[2], BF16_SHAPES[5]], ids=lambda w: w.name)
 def test_bwd_alone_from_oracle_forward(w):
     """The backward fed the oracle's O (rounded to bf16) and LSE, so that its
@@ -127,7 +168,7 @@ def test_determinism_bitwise():
 def test_n_zero_gives_zero_key_gradients():
     """No queries: dK and dV are empty sums, i.e. zero."""
     dev = "cuda:0"
-    for dtype in (torch.bfloat16, torch.float32):
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
         q = torch.empty(1, 2, 0, 64, dtype=dtype, device=dev)
         k = torch.randn(1, 2, 70, 64, device=dev).to(dtype)
         v = torch.randn(1, 2, 70, 64, device=dev).to(dtype)

@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 # Values of include/attn.h.
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
+_DTYPE_CODES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
 ATTN_DQ_AUTO, ATTN_DQ_SEPARATE = 0, 1
 ATTN_STAGE_PREPROCESS, ATTN_STAGE_DKDV, ATTN_STAGE_DQ = 1 << 8, 1 << 9, 1 << 10
@@ -65,11 +66,10 @@ def status_str(status: int) -> str:
 
 
 def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
-        return ATTN_BF16
-    if t.dtype == torch.float32:
-        return ATTN_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16, float16 or float32")
+    return code
 
 
 def _ptr(t):
@@ -118,7 +118,9 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
 
 
 def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto"):
-    code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
+    code = _DTYPE_CODES.get(dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {dtype}; use bfloat16, float16 or float32")
     return int(load().attn_bwd_workspace_bytes(B, H, n, m, d, dv, code, DQ_MODES[dq_mode]))
 
 

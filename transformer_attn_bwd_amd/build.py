@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip",
+SOURCES = ["attn_api.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip",
            "attn_f32.hip"]
 ARCH = "gfx950"
 

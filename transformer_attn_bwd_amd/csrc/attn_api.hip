@@ -19,15 +19,21 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+bool is_16bit(int dtype) { return dtype == ATTN_BF16 || dtype == ATTN_F16; }
+
+static_assert(ATTN_F32 == attn::kDtypeF32 && ATTN_BF16 == attn::kDtypeBF16 &&
+                  ATTN_F16 == attn::kDtypeF16,
+              "dtype codes of the C ABI and the kernels agree");
+
 // Sizes, dtype, head widths, causal shape and scale; shared by fwd and bwd.
 int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int causal, int dtype,
                   Problem* out) {
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_EUNSUPPORTED;
     if (B < 0 || H < 0 || n < 0 || m < 1 || d < 1 || dv < 1) return ATTN_EINVAL;
     if (!isfinite(scale)) return ATTN_EINVAL;
     if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
     if (n > kMaxSeq || m > kMaxSeq) return ATTN_EUNSUPPORTED;
-    if (dtype == ATTN_BF16) {
+    if (is_16bit(dtype)) {
         const bool ok = (d == 64 && dv == 64) || (d == 128 && dv == 128) || (d == 128 && dv == 64);
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((long)B * H > 0x7fffffffL) return ATTN_EUNSUPPORTED;
@@ -48,11 +54,11 @@ int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int ca
 }
 
 // A tensor with elements needs a non-null pointer aligned for the kernels'
-// vector accesses (16 bytes for bf16 rows, 4 bytes for float32).
+// vector accesses (16 bytes for 16-bit rows, 4 bytes for float32).
 bool tensor_ok(const void* p, long elems, int dtype) {
     if (elems == 0) return true;
     if (p == nullptr) return false;
-    return aligned(p, dtype == ATTN_BF16 ? 16 : 4);
+    return aligned(p, is_16bit(dtype) ? 16 : 4);
 }
 
 size_t workspace_bytes(const Problem& p) {
@@ -97,8 +103,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (hq == 0) return ATTN_OK;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    bool ok = dtype == ATTN_BF16
-                  ? attn::launch_fwd_bf16(p, q, k, v, o, lse, s)
+    bool ok = is_16bit(dtype)
+                  ? attn::launch_fwd_mfma(p, q, k, v, o, lse, s)
                   : attn::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                          (float*)o, lse, s);
     if (!ok) return ATTN_EUNSUPPORTED;
@@ -146,24 +152,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
 
-    const bool bf = dtype == ATTN_BF16;
+    const bool bf = is_16bit(dtype);
     bool ok = true;
     if (n > 0 && (stages & ATTN_STAGE_PREPROCESS)) {
-        ok = bf ? attn::launch_bwd_preprocess_bf16(p, o, dout, lse, w, s)
+        ok = bf ? attn::launch_bwd_preprocess_mfma(p, o, dout, lse, w, s)
                 : attn::launch_bwd_preprocess_f32(p, (const float*)o, (const float*)dout, lse, w, s);
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     if (stages & ATTN_STAGE_DKDV) {
         // With n == 0 the kernel visits no query tile and writes zeros.
-        ok = bf ? attn::launch_bwd_dkdv_bf16(p, q, k, v, dout, w, dk, dv_out, s)
+        ok = bf ? attn::launch_bwd_dkdv_mfma(p, q, k, v, dout, w, dk, dv_out, s)
                 : attn::launch_bwd_dkdv_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                             (const float*)dout, w, (float*)dk, (float*)dv_out, s);
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     if (n > 0 && (stages & ATTN_STAGE_DQ)) {
-        ok = bf ? attn::launch_bwd_dq_bf16(p, q, k, v, dout, w, dq, s)
+        ok = bf ? attn::launch_bwd_dq_mfma(p, q, k, v, dout, w, dq, s)
                 : attn::launch_bwd_dq_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                           (const float*)dout, w, (float*)dq, s);
         if (!ok) return ATTN_EUNSUPPORTED;

@@ -1,4 +1,5 @@
-// dQ of backward attention on bf16 MFMA (float32 accumulation).
+// dQ of backward attention on 16-bit MFMA (bf16 or f16 inputs, float32
+// accumulation).
 //
 // For query row i, dQ_i = scale * sum_j dS_ij K_j with dS = P o (dP - D)
 // and dP = dO V^T ("Attention Backpropagation: Step by step derivation",
@@ -33,26 +34,26 @@ struct DqCfg {
     static constexpr int PD = 4;              // operand reads issued ahead
 };
 
-template <int D, int DV, bool CAUSAL>
+template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ Dw, bf16* __restrict__ dq, int n, int m, int n_pad, float scale,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ Dw, T* __restrict__ dq, int n, int m, int n_pad, float scale,
     float c2) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     // One LDS variable per buffer: the compiler can then tell that reads
     // of one buffer do not alias the asynchronous fills of the other, and
     // does not make them wait for those fills.
-    __shared__ __align__(1024) bf16 sK0[BN * D];
-    __shared__ __align__(1024) bf16 sK1[BN * D];
-    __shared__ __align__(1024) bf16 sV0[BN * DV];
-    __shared__ __align__(1024) bf16 sV1[BN * DV];
-    auto Kbuf = [&](auto b_) __attribute__((always_inline)) -> bf16* {
+    __shared__ __align__(1024) T sK0[BN * D];
+    __shared__ __align__(1024) T sK1[BN * D];
+    __shared__ __align__(1024) T sV0[BN * DV];
+    __shared__ __align__(1024) T sV1[BN * DV];
+    auto Kbuf = [&](auto b_) __attribute__((always_inline)) -> T* {
         if constexpr (decltype(b_)::value == 0) return sK0;
         else return sK1;
     };
-    auto Vbuf = [&](auto b_) __attribute__((always_inline)) -> bf16* {
+    auto Vbuf = [&](auto b_) __attribute__((always_inline)) -> T* {
         if constexpr (decltype(b_)::value == 0) return sV0;
         else return sV1;
     };
@@ -63,17 +64,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
     const int i0 = qb * C::BM;
 
-    const bf16* qh = q + bh * (long)n * D;
-    const bf16* kh = k + bh * (long)m * D;
-    const bf16* vh = v + bh * (long)m * DV;
-    const bf16* oh = dout + bh * (long)n * DV;
+    const T* qh = q + bh * (long)n * D;
+    const T* kh = k + bh * (long)m * D;
+    const T* vh = v + bh * (long)m * DV;
+    const T* oh = dout + bh * (long)n * DV;
 
     // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31).
     // Taking one tile from each half of the workgroup's rows gives every
     // wave the same share of the masked diagonal work.  Rows past n load
     // zeros and LSE2 = +inf, so their P, dS and dQ contributions vanish.
     int myq[2];
-    bf16x8 qreg[2][D / 16], oreg[2][DV / 16];
+    vec8<T> qreg[2][D / 16], oreg[2][DV / 16];
     float l2[2], Dq[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -81,10 +82,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const bool ok = myq[t] < n;
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc)
-            qreg[t][kc] = ok ? gload_bf16x8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : bf16x8{};
+            qreg[t][kc] = ok ? gload8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : vec8<T>{};
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
-            oreg[t][kc] = ok ? gload_bf16x8(oh + (long)myq[t] * DV + 16 * kc + 8 * g) : bf16x8{};
+            oreg[t][kc] = ok ? gload8(oh + (long)myq[t] * DV + 16 * kc + 8 * g) : vec8<T>{};
         // Q and dO rows are only MFMA inputs: keep them in AGPRs, leaving
         // the VGPRs to the S, dP and dS tiles of a 64-key step
 #pragma unroll
@@ -139,13 +140,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // the dQ products of chunk c.
     auto compute = [&](auto buf_, auto masked_, int k0) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_)::value;
-        const bf16* Ks = Kbuf(buf_);
-        const bf16* Vs = Vbuf(buf_);
+        const T* Ks = Kbuf(buf_);
+        const T* Vs = Vbuf(buf_);
         constexpr int KA = D / 16, KB = DV / 16, NX = D / 32;
         constexpr int NKH = BN / 32, NC = 2 * NKH;
         constexpr int FV = NKH * KA, FT = FV + NKH * KB, NF = FT + NC * NX;
 
-        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
+        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> vec8<T> {
             constexpr int f = decltype(f_)::value;
             if constexpr (f < FV) {
                 return tile_read8_at<D>(Ks, toK, 32 * (f / KA), f % KA);
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         };
 
         f32x16 S[NKH][2], dP[NKH][2];
-        bf16x8 dSb[NKH][2][2];
+        vec8<T> dSb[NKH][2][2];
 
         int lim[2];
         if constexpr (MASKED) {
@@ -185,16 +186,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int s = 0; s < 8; ++s)
                 d8[s] = S[kh][t][8 * h + s] * (dP[kh][t][8 * h + s] - Dq[t]);
-            dSb[kh][t][h] = pack8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
+            dSb[kh][t][h] = pack8<T>(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
         };
 
-        bf16x8 fr[PD];
+        vec8<T> fr[PD];
         static_for<PD>([&](auto f_) { fr[decltype(f_)::value] = load_frag(f_); });
         __builtin_amdgcn_sched_barrier(0);
 
         static_for<NF>([&](auto f_) {
             constexpr int f = decltype(f_)::value;
-            const bf16x8 cur = fr[f % PD];
+            const vec8<T> cur = fr[f % PD];
             if constexpr (f + PD < NF) fr[f % PD] = load_frag(std::integral_constant<int, f + PD>{});
             if constexpr (f < FV) {
                 constexpr int kh = f / KA, r = f % KA;
@@ -274,46 +275,54 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (myq[t] < n) {
-            bf16* qrow = dq + (bh * (long)n + myq[t]) * D;
+            T* qrow = dq + (bh * (long)n + myq[t]) * D;
 #pragma unroll
             for (int x = 0; x < D / 32; ++x) {
 #pragma unroll
                 for (int vq = 0; vq < 4; ++vq) {
-                    bf16x4 w;
+                    vec4<T> w;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[x][t][4 * vq + r] * scale);
-                    *reinterpret_cast<bf16x4*>(qrow + 32 * x + 8 * vq + 4 * g) = w;
+                    for (int r = 0; r < 4; ++r) w[r] = (T)(acc[x][t][4 * vq + r] * scale);
+                    *reinterpret_cast<vec4<T>*>(qrow + 32 * x + 8 * vq + 4 * g) = w;
                 }
             }
         }
     }
 }
 
-template <int D, int DV>
+template <typename T, int D, int DV>
 void launch_dq(const Problem& p, const void* q, const void* k, const void* v, const void* dout,
                const Workspace& w, void* dq, hipStream_t s) {
     using C = DqCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
     if (p.causal)
-        bwd_dq_kernel<D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
-            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+        bwd_dq_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
+            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
+            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2);
     else
-        bwd_dq_kernel<D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
-            (bf16*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+        bwd_dq_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
+            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
+            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+}
+
+template <typename T>
+bool dq_for_widths(const Problem& p, const void* q, const void* k, const void* v,
+                   const void* dout, const Workspace& w, void* dq, hipStream_t s) {
+    if (p.d == 64 && p.dv == 64) launch_dq<T, 64, 64>(p, q, k, v, dout, w, dq, s);
+    else if (p.d == 128 && p.dv == 128) launch_dq<T, 128, 128>(p, q, k, v, dout, w, dq, s);
+    else if (p.d == 128 && p.dv == 64) launch_dq<T, 128, 64>(p, q, k, v, dout, w, dq, s);
+    else return false;
+    return true;
 }
 
 }  // namespace
 
-bool launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const Workspace& w, void* dq, hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch_dq<64, 64>(p, q, k, v, dout, w, dq, s);
-    else if (p.d == 128 && p.dv == 128) launch_dq<128, 128>(p, q, k, v, dout, w, dq, s);
-    else if (p.d == 128 && p.dv == 64) launch_dq<128, 64>(p, q, k, v, dout, w, dq, s);
-    else return false;
-    return true;
+    if (p.dtype == kDtypeBF16) return dq_for_widths<bf16>(p, q, k, v, dout, w, dq, s);
+    if (p.dtype == kDtypeF16) return dq_for_widths<f16>(p, q, k, v, dout, w, dq, s);
+    return false;
 }
 
 }  // namespace attn

@@ -1,5 +1,6 @@
-// Backward attention on bf16 MFMA (float32 accumulation): the preprocess
-// and dK/dV kernels (the dQ pass is in attn_bwd_dq_bf16.hip).
+// Backward attention on 16-bit MFMA (bf16 or f16 inputs, float32
+// accumulation): the preprocess and dK/dV kernels (the dQ pass is in
+// attn_bwd_dq_mfma.hip).
 //
 //  1. preprocess: D_i = rowsum(dO o O)_i, the cheap form of rowsum(dP o P)
 //     (step-by-step derivation, "Gradient of S"; mlgrind "Follow-up"), and
@@ -24,9 +25,9 @@ namespace {
 
 // ---------------------------------------------------------------- preprocess
 
-template <int DV>
+template <typename T, int DV>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
-    const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ lse2, float* __restrict__ Dw, int n, int n_pad, long total_rows) {
     constexpr int LPR = DV / 8;        // lanes per row, 8 elements (16 bytes) each
     constexpr int RPB = 256 / LPR;     // rows per block
@@ -39,8 +40,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     float acc = 0.f;
     if (valid_row && i < n) {
         const long off = (bh * (long)n + i) * DV + 8 * part;
-        bf16x8 a = gload_bf16x8(o + off);
-        bf16x8 b = gload_bf16x8(dout + off);
+        vec8<T> a = gload8(o + off);
+        vec8<T> b = gload8(dout + off);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
     }
@@ -95,7 +96,7 @@ struct DkdvSched {
     }
     // Softmax elements, 32 per step per lane: element i is accumulator
     // slot e(i) of key tile kt(i); ordered by 8-slot operand chunk, so
-    // that each bf16 operand is complete early.
+    // that each 16-bit operand is complete early.
     static constexpr int elem_c(int i) { return i / 16; }
     static constexpr int elem_kt(int i) { return (i / 8) % 2; }
     static constexpr int elem_e(int i) { return 8 * elem_c(i) + i % 8; }
@@ -116,11 +117,11 @@ struct DkdvSched {
 // query tiles (32 rows of Q and dO, with their LSE2 and D) stream through
 // two LDS buffers.  Each Q, dO, Q^T and dO^T fragment read from LDS feeds
 // two MFMAs (the wave's two key tiles).  dK and dV accumulate in AGPRs.
-template <int D, int DV, bool CAUSAL>
+template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ Dw, bf16* __restrict__ dk, bf16* __restrict__ dvo, int n, int m,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ Dw, T* __restrict__ dk, T* __restrict__ dvo, int n, int m,
     int n_pad, float scale, float c2) {
     using C = DkdvCfg<D, DV>;
     using SC = DkdvSched<D, DV>;
@@ -128,11 +129,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // One LDS variable per buffer: the compiler can then tell that reads
     // of one buffer do not alias the asynchronous fills of the other, and
     // does not make them wait for those fills.
-    __shared__ __align__(1024) bf16 sK[C::BN * D];
-    __shared__ __align__(1024) bf16 sQ0[BM * D];
-    __shared__ __align__(1024) bf16 sQ1[BM * D];
-    __shared__ __align__(1024) bf16 sO0[BM * DV];
-    __shared__ __align__(1024) bf16 sO1[BM * DV];
+    __shared__ __align__(1024) T sK[C::BN * D];
+    __shared__ __align__(1024) T sQ0[BM * D];
+    __shared__ __align__(1024) T sQ1[BM * D];
+    __shared__ __align__(1024) T sO0[BM * DV];
+    __shared__ __align__(1024) T sO1[BM * DV];
     __shared__ __align__(256) float sL0[64];
     __shared__ __align__(256) float sL1[64];
     __shared__ __align__(256) float sD0[64];
@@ -148,10 +149,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int j0 = blockIdx.y * C::BN;
     const int kw0 = j0 + C::KW * wave;      // this wave's first key
 
-    const bf16* qh = q + bh * (long)n * D;
-    const bf16* kh = k + bh * (long)m * D;
-    const bf16* vh = v + bh * (long)m * DV;
-    const bf16* oh = dout + bh * (long)n * DV;
+    const T* qh = q + bh * (long)n * D;
+    const T* kh = k + bh * (long)m * D;
+    const T* vh = v + bh * (long)m * DV;
+    const T* oh = dout + bh * (long)n * DV;
     const float* lh = lse2 + bh * (long)n_pad;
     const float* dh = Dw + bh * (long)n_pad;
 
@@ -164,20 +165,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     // This lane's V row for key tile kt (key kw0 + 32 kt + li): B operand of
     // dP = dO V^T.
-    bf16x8 vreg[2][DV / 16];
+    vec8<T> vreg[2][DV / 16];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
         const int key = kw0 + 32 * kt + li;
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
-            vreg[kt][kc] = key < m ? gload_bf16x8(vh + (long)key * DV + 16 * kc + 8 * g) : bf16x8{};
+            vreg[kt][kc] = key < m ? gload8(vh + (long)key * DV + 16 * kc + 8 * g) : vec8<T>{};
     }
 
     TileOffsets<D> toQ;
     toQ.init(lane);
     TileOffsets<DV> toO;
     toO.init(lane);
-    const bf16* Kw = sK + C::KW * wave * D;  // this wave's 64 K rows
+    const T* Kw = sK + C::KW * wave * D;  // this wave's 64 K rows
 
     const int i_begin = CAUSAL ? j0 : 0;
     const int i_end = (n + BM - 1) / BM * BM;
@@ -223,12 +224,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // apply the causal mask.
     auto compute = [&](auto buf_, auto masked_, int i0) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_)::value;
-        const bf16* Qs = pick(buf_, sQ0, sQ1);
-        const bf16* Os = pick(buf_, sO0, sO1);
+        const T* Qs = pick(buf_, sQ0, sQ1);
+        const T* Os = pick(buf_, sO0, sO1);
         const float* Ls = pick(buf_, sL0, sL1);
         const float* Ds = pick(buf_, sD0, sD1);
 
-        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
+        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> vec8<T> {
             constexpr int f = decltype(f_)::value;
             if constexpr (f < SC::F_K) {
                 return tile_read8_at<D>(Qs, toQ, 0, f);
@@ -247,9 +248,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         };
 
         f32x16 S[2], dP[2];          // S is overwritten by P
-        bf16x8 Pb[2][2], dSb[2][2];
+        vec8<T> Pb[2][2], dSb[2][2];
         f32x4 l4[4], d4[4];
-        bf16x8 fr[SC::NF];
+        vec8<T> fr[SC::NF];
 
         // Query of accumulator slot e: i0 + 8(e>>2) + 4g + (e&3); key of
         // tile kt: kw0 + 32kt + li.  The slot is masked when key > query,
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             S[kt][e] = pv;
             if constexpr (i % 8 == 7) {
                 constexpr int c = SC::elem_c(i), b = 8 * c;
-                Pb[kt][c] = pack8(S[kt][b], S[kt][b + 1], S[kt][b + 2], S[kt][b + 3], S[kt][b + 4],
+                Pb[kt][c] = pack8<T>(S[kt][b], S[kt][b + 1], S[kt][b + 2], S[kt][b + 3], S[kt][b + 4],
                                   S[kt][b + 5], S[kt][b + 6], S[kt][b + 7]);
             }
         };
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             dP[kt][e] = S[kt][e] * (dP[kt][e] - d4[vq][r]);
             if constexpr (i % 8 == 7) {
                 constexpr int c = SC::elem_c(i), b = 8 * c;
-                dSb[kt][c] = pack8(dP[kt][b], dP[kt][b + 1], dP[kt][b + 2], dP[kt][b + 3],
+                dSb[kt][c] = pack8<T>(dP[kt][b], dP[kt][b + 1], dP[kt][b + 2], dP[kt][b + 3],
                                    dP[kt][b + 4], dP[kt][b + 5], dP[kt][b + 6], dP[kt][b + 7]);
             }
         };
@@ -369,8 +370,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Accumulator slot vv of tile (kt, x) holds key kw0 + 32kt + 8(vv>>2) +
     // 4g + (vv&3), column 32x + li.
-    bf16* dkh = dk + bh * (long)m * D;
-    bf16* dvh = dvo + bh * (long)m * DV;
+    T* dkh = dk + bh * (long)m * D;
+    T* dvh = dvo + bh * (long)m * DV;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -379,59 +380,75 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             if (key < m) {
 #pragma unroll
                 for (int x = 0; x < D / 32; ++x)
-                    dkh[(long)key * D + 32 * x + li] = (bf16)(accK[kt][x][vv] * scale);
+                    dkh[(long)key * D + 32 * x + li] = (T)(accK[kt][x][vv] * scale);
 #pragma unroll
                 for (int x = 0; x < DV / 32; ++x)
-                    dvh[(long)key * DV + 32 * x + li] = (bf16)accV[kt][x][vv];
+                    dvh[(long)key * DV + 32 * x + li] = (T)accV[kt][x][vv];
             }
         }
     }
 }
 
-template <int DV>
+template <typename T, int DV>
 void launch_pre(const Problem& p, const void* o, const void* dout, const float* lse,
                 const Workspace& w, hipStream_t s) {
     constexpr int RPB = 256 / (DV / 8);
     const long total = p.heads() * (long)w.n_pad;
     const unsigned blocks = (unsigned)((total + RPB - 1) / RPB);
-    bwd_preprocess_kernel<DV><<<blocks, 256, 0, s>>>((const bf16*)o, (const bf16*)dout, lse,
-                                                     w.lse2, w.D, p.n, w.n_pad, total);
+    bwd_preprocess_kernel<T, DV><<<blocks, 256, 0, s>>>((const T*)o, (const T*)dout, lse,
+                                                        w.lse2, w.D, p.n, w.n_pad, total);
 }
 
-template <int D, int DV>
+template <typename T, int D, int DV>
 void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
                  const void* dout, const Workspace& w, void* dk, void* dv, hipStream_t s) {
     using C = DkdvCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.m + C::BN - 1) / C::BN));
     const float c2 = p.scale * kLog2e;
     if (p.causal)
-        bwd_dkdv_kernel<D, DV, true><<<grid, 256, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
-            (bf16*)dk, (bf16*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+        bwd_dkdv_kernel<T, D, DV, true><<<grid, 256, 0, s>>>(
+            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
+            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2);
     else
-        bwd_dkdv_kernel<D, DV, false><<<grid, 256, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, w.lse2, w.D,
-            (bf16*)dk, (bf16*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+        bwd_dkdv_kernel<T, D, DV, false><<<grid, 256, 0, s>>>(
+            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
+            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+}
+
+template <typename T>
+bool dkdv_for_widths(const Problem& p, const void* q, const void* k, const void* v,
+                     const void* dout, const Workspace& w, void* dk, void* dv, hipStream_t s) {
+    if (p.d == 64 && p.dv == 64) launch_dkdv<T, 64, 64>(p, q, k, v, dout, w, dk, dv, s);
+    else if (p.d == 128 && p.dv == 128) launch_dkdv<T, 128, 128>(p, q, k, v, dout, w, dk, dv, s);
+    else if (p.d == 128 && p.dv == 64) launch_dkdv<T, 128, 64>(p, q, k, v, dout, w, dk, dv, s);
+    else return false;
+    return true;
+}
+
+template <typename T>
+bool pre_for_widths(const Problem& p, const void* o, const void* dout, const float* lse,
+                    const Workspace& w, hipStream_t s) {
+    if (p.dv == 64) launch_pre<T, 64>(p, o, dout, lse, w, s);
+    else if (p.dv == 128) launch_pre<T, 128>(p, o, dout, lse, w, s);
+    else return false;
+    return true;
 }
 
 }  // namespace
 
-bool launch_bwd_preprocess_bf16(const Problem& p, const void* o, const void* dout,
+bool launch_bwd_preprocess_mfma(const Problem& p, const void* o, const void* dout,
                                 const float* lse, const Workspace& w, hipStream_t s) {
-    if (p.dv == 64) launch_pre<64>(p, o, dout, lse, w, s);
-    else if (p.dv == 128) launch_pre<128>(p, o, dout, lse, w, s);
-    else return false;
-    return true;
+    if (p.dtype == kDtypeBF16) return pre_for_widths<bf16>(p, o, dout, lse, w, s);
+    if (p.dtype == kDtypeF16) return pre_for_widths<f16>(p, o, dout, lse, w, s);
+    return false;
 }
 
-bool launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
                           const void* dout, const Workspace& w, void* dk, void* dv,
                           hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch_dkdv<64, 64>(p, q, k, v, dout, w, dk, dv, s);
-    else if (p.d == 128 && p.dv == 128) launch_dkdv<128, 128>(p, q, k, v, dout, w, dk, dv, s);
-    else if (p.d == 128 && p.dv == 64) launch_dkdv<128, 64>(p, q, k, v, dout, w, dk, dv, s);
-    else return false;
-    return true;
+    if (p.dtype == kDtypeBF16) return dkdv_for_widths<bf16>(p, q, k, v, dout, w, dk, dv, s);
+    if (p.dtype == kDtypeF16) return dkdv_for_widths<f16>(p, q, k, v, dout, w, dk, dv, s);
+    return false;
 }
 
 }  // namespace attn

@@ -1,4 +1,5 @@
-// Forward attention on bf16 MFMA with float32 softmax statistics; emits O
+// Forward attention on 16-bit MFMA (bf16 or f16 inputs, float32
+// accumulation and softmax statistics); emits O
 // and the per-row log-sum-exp that the backward uses to recompute P
 // (mlgrind "Forward"; "Attention Backpropagation: Step by step
 // derivation", section Forward Pass).
@@ -34,19 +35,19 @@ struct FwdCfg {
 
 constexpr float kRescaleThreshold = 8.f;     // log2 of the largest P allowed
 
-template <int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int n, int m, float c2) {
+template <typename T, int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    T* __restrict__ o, float* __restrict__ lse, int n, int m, float c2) {
     using C = FwdCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     constexpr int KA = D / 16, NXV = DV / 32;
     // One LDS variable per buffer: reads of one buffer are then known not
     // to alias the asynchronous fills of the other.
-    __shared__ __align__(1024) bf16 sK0[BN * D];
-    __shared__ __align__(1024) bf16 sK1[BN * D];
-    __shared__ __align__(1024) bf16 sV0[BN * DV];
-    __shared__ __align__(1024) bf16 sV1[BN * DV];
+    __shared__ __align__(1024) T sK0[BN * D];
+    __shared__ __align__(1024) T sK1[BN * D];
+    __shared__ __align__(1024) T sV0[BN * DV];
+    __shared__ __align__(1024) T sV1[BN * DV];
     auto pick = [](auto b_, auto* x0, auto* x1) __attribute__((always_inline)) {
         if constexpr (decltype(b_)::value == 0) return x0;
         else return x1;
@@ -58,9 +59,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
     const int i0 = qb * C::BM;
 
-    const bf16* qh = q + bh * (long)n * D;
-    const bf16* kh = k + bh * (long)m * D;
-    const bf16* vh = v + bh * (long)m * DV;
+    const T* qh = q + bh * (long)n * D;
+    const T* kh = k + bh * (long)m * D;
+    const T* vh = v + bh * (long)m * DV;
 
     // A negative scale is handled by negating Q, so that the row max of
     // S * c2 is c2 times the row max of the computed S.
@@ -70,15 +71,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31), one
     // tile from each half of the workgroup's rows (even causal work).
     int myq[2];
-    bf16x8 qreg[2][KA];
+    vec8<T> qreg[2][KA];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         myq[t] = i0 + (C::BM / 2) * t + 32 * wave + li;
         const bool ok = myq[t] < n;
 #pragma unroll
         for (int kc = 0; kc < KA; ++kc) {
-            bf16x8 x = ok ? gload_bf16x8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : bf16x8{};
-            if (neg) x = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
+            vec8<T> x = ok ? gload8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : vec8<T>{};
+            if (neg) x = __builtin_bit_cast(vec8<T>, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
             qreg[t][kc] = x;
             // keep the Q operands in AGPRs (MFMAs read them from there), so
             // that the VGPRs hold the four S tiles of a step
@@ -129,11 +130,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr bool MASKED = decltype(masked_)::value;
         constexpr int NKH = BN / 32;                    // 32-key halves per step
         constexpr int NC = 2 * NKH;                     // 16-key chunks per step
-        const bf16* Ks = pick(buf_, sK0, sK1);
-        const bf16* Vs = pick(buf_, sV0, sV1);
+        const T* Ks = pick(buf_, sK0, sK1);
+        const T* Vs = pick(buf_, sV0, sV1);
         constexpr int NF = NKH * KA + NC * NXV;
 
-        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> bf16x8 {
+        auto load_frag = [&](auto f_) __attribute__((always_inline)) -> vec8<T> {
             constexpr int f = decltype(f_)::value;
             if constexpr (f < NKH * KA) {
                 return tile_read8_at<D>(Ks, toK, 32 * (f / KA), f % KA);
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         };
 
         f32x16 S[NKH][2];
-        bf16x8 Pb[NC][2];
+        vec8<T> Pb[NC][2];
         float mb[2];
         int lim[2];
         if constexpr (MASKED) {
@@ -200,16 +201,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 p8[s] = pv;
                 l_run[t] += pv;
             }
-            Pb[c][t] = pack8(p8[0], p8[1], p8[2], p8[3], p8[4], p8[5], p8[6], p8[7]);
+            Pb[c][t] = pack8<T>(p8[0], p8[1], p8[2], p8[3], p8[4], p8[5], p8[6], p8[7]);
         };
 
-        bf16x8 fr[PD];
+        vec8<T> fr[PD];
         static_for<PD>([&](auto f_) { fr[decltype(f_)::value] = load_frag(f_); });
         __builtin_amdgcn_sched_barrier(0);
 
         static_for<NF>([&](auto f_) {
             constexpr int f = decltype(f_)::value;
-            const bf16x8 cur = fr[f % PD];
+            const vec8<T> cur = fr[f % PD];
             if constexpr (f + PD < NF) fr[f % PD] = load_frag(std::integral_constant<int, f + PD>{});
             if constexpr (f < NKH * KA) {
                 constexpr int kh = f / KA, r = f % KA;
@@ -282,15 +283,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const float l_tot = l_run[t] + xor_lane32(l_run[t]);
         const float inv = 1.f / l_tot;
         if (myq[t] < n) {
-            bf16* orow = o + (bh * (long)n + myq[t]) * DV;
+            T* orow = o + (bh * (long)n + myq[t]) * DV;
 #pragma unroll
             for (int x = 0; x < NXV; ++x) {
 #pragma unroll
                 for (int vq = 0; vq < 4; ++vq) {
-                    bf16x4 w;
+                    vec4<T> w;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[x][t][4 * vq + r] * inv);
-                    *reinterpret_cast<bf16x4*>(orow + 32 * x + 8 * vq + 4 * g) = w;
+                    for (int r = 0; r < 4; ++r) w[r] = (T)(acc[x][t][4 * vq + r] * inv);
+                    *reinterpret_cast<vec4<T>*>(orow + 32 * x + 8 * vq + 4 * g) = w;
                 }
             }
             if (g == 0) lse[bh * (long)n + myq[t]] = (m_run[t] + log2f(l_tot)) * kLn2;
@@ -298,29 +299,37 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 }
 
-template <int D, int DV>
+template <typename T, int D, int DV>
 void launch(const Problem& p, const void* q, const void* k, const void* v, void* o,
             float* lse, hipStream_t s) {
     using C = FwdCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
     if (p.causal)
-        fwd_bf16_kernel<D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.n, p.m, c2);
+        fwd_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
+            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2);
     else
-        fwd_bf16_kernel<D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
-            (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.n, p.m, c2);
+        fwd_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
+            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2);
+}
+
+template <typename T>
+bool fwd_for_widths(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                    float* lse, hipStream_t s) {
+    if (p.d == 64 && p.dv == 64) launch<T, 64, 64>(p, q, k, v, o, lse, s);
+    else if (p.d == 128 && p.dv == 128) launch<T, 128, 128>(p, q, k, v, o, lse, s);
+    else if (p.d == 128 && p.dv == 64) launch<T, 128, 64>(p, q, k, v, o, lse, s);
+    else return false;
+    return true;
 }
 
 }  // namespace
 
-bool launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+bool launch_fwd_mfma(const Problem& p, const void* q, const void* k, const void* v, void* o,
                      float* lse, hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch<64, 64>(p, q, k, v, o, lse, s);
-    else if (p.d == 128 && p.dv == 128) launch<128, 128>(p, q, k, v, o, lse, s);
-    else if (p.d == 128 && p.dv == 64) launch<128, 64>(p, q, k, v, o, lse, s);
-    else return false;
-    return true;
+    if (p.dtype == kDtypeBF16) return fwd_for_widths<bf16>(p, q, k, v, o, lse, s);
+    if (p.dtype == kDtypeF16) return fwd_for_widths<f16>(p, q, k, v, o, lse, s);
+    return false;
 }
 
 }  // namespace attn

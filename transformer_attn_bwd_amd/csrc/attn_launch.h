@@ -6,6 +6,11 @@
 
 namespace attn {
 
+// Element types, the values of enum attn_dtype in attn.h.
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+constexpr int kDtypeF16 = 2;
+
 struct Problem {
     long B = 0, H = 0;
     int n = 0, m = 0, d = 0, dv = 0;
@@ -27,15 +32,16 @@ struct Workspace {
     int n_pad;
 };
 
-// bf16 MFMA path; return false if (d, dv) has no instantiation.
-bool launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v, void* o,
+// 16-bit MFMA path (p.dtype kDtypeBF16 or kDtypeF16); return false if
+// (d, dv) or the dtype has no instantiation.
+bool launch_fwd_mfma(const Problem& p, const void* q, const void* k, const void* v, void* o,
                      float* lse, hipStream_t s);
-bool launch_bwd_preprocess_bf16(const Problem& p, const void* o, const void* dout,
+bool launch_bwd_preprocess_mfma(const Problem& p, const void* o, const void* dout,
                                 const float* lse, const Workspace& w, hipStream_t s);
-bool launch_bwd_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
                           const void* dout, const Workspace& w, void* dk, void* dv,
                           hipStream_t s);
-bool launch_bwd_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const Workspace& w, void* dq, hipStream_t s);
 
 // fp32 path (one wave per row; any d, dv in 1..128).

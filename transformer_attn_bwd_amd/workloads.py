@@ -9,7 +9,7 @@ i.i.d. standard normal float32 values with ``torch.randn`` in the order
 Q [B,H,n,d], K [B,H,m,d], V [B,H,m,dv], dO [B,H,n,dv]; Q and K are then
 multiplied by ``qk_mult`` (3.0 for the cross-attention stress case, so raw
 logits reach about +-100) and every tensor is rounded to the workload's
-dtype (round to nearest even for bfloat16).
+dtype (round to nearest even for bfloat16 and float16).
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ class Workload:
     m: int
     d: int
     dv: int
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32", "bf16" or "fp16"
     causal: bool
     seed: int
     qk_mult: float = 1.0
@@ -40,7 +40,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+        return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[self.dtype]
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -60,6 +60,9 @@ WORKLOADS = {
     "causal_16k_d128": Workload("causal_16k_d128", 1, 32, 16384, 16384, 128, 128, "bf16", True, 3),
     "cross_512x2048_d128_dv64": Workload("cross_512x2048_d128_dv64", 8, 16, 512, 2048, 128, 64,
                                          "bf16", False, 4, qk_mult=3.0),
+    # the headline shape with IEEE half inputs (same seed, rounded to float16)
+    "causal_4k_d128_fp16": Workload("causal_4k_d128_fp16", 2, 32, 4096, 4096, 128, 128, "fp16",
+                                    True, 2),
 }
 HEADLINE = "causal_4k_d128"
 
