@@ -69,9 +69,11 @@ def _load():
     lib.oracle_attn_fwd.restype = I
     lib.oracle_attn_bwd.argtypes = [dp] * 12 + [L] * 6 + [D, I, I]
     lib.oracle_attn_bwd.restype = I
-    lib.oracle_attn_rows.argtypes = [dp, dp, dp, dp, L, L, L, L, D, I, lp, L, dp, dp, dp, dp]
+    lib.oracle_attn_bwd_masked.argtypes = [dp] * 10 + [L] * 6 + [D, I, lp, lp]
+    lib.oracle_attn_bwd_masked.restype = I
+    lib.oracle_attn_rows.argtypes = [dp, dp, dp, dp, L, L, L, L, D, I, L, lp, L, dp, dp, dp, dp]
     lib.oracle_attn_rows.restype = I
-    lib.oracle_attn_cols.argtypes = [dp, dp, dp, dp, L, L, L, L, D, I, lp, L, dp, dp]
+    lib.oracle_attn_cols.argtypes = [dp, dp, dp, dp, L, L, L, L, D, I, L, lp, L, dp, dp]
     lib.oracle_attn_cols.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
@@ -172,8 +174,9 @@ def attn_bwd(q, k, v, dout, scale=None, causal=False, variant=EXACT, want_ds=Fal
     return out
 
 
-def attn_rows(q, k, v, dout, rows, scale=None, causal=False):
-    """One head: O, LSE, D and dQ for the listed query rows only."""
+def attn_rows(q, k, v, dout, rows, scale=None, causal=False, causal_offset=0):
+    """One head: O, LSE, D and dQ for the listed query rows only.  Under the
+    causal mask key j is visible from row i when j <= i + causal_offset."""
     q, k, v, do = (_f64(t) for t in (q, k, v, dout))
     n, d = q.shape
     m, dv = v.shape
@@ -184,14 +187,16 @@ def attn_rows(q, k, v, dout, rows, scale=None, causal=False):
     o = np.zeros((r, dv)); lse = np.zeros(r); D = np.zeros(r); dq = np.zeros((r, d))
     rc = _load().oracle_attn_rows(
         _ptr(q), _ptr(k), _ptr(v), _ptr(do), n, m, d, dv, float(scale), int(bool(causal)),
-        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), r, _ptr(o), _ptr(lse), _ptr(D), _ptr(dq))
+        int(causal_offset), rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), r, _ptr(o),
+        _ptr(lse), _ptr(D), _ptr(dq))
     if rc:
         raise ValueError("oracle_attn_rows: invalid arguments")
     return {"o": o, "lse": lse, "D": D, "dq": dq}
 
 
-def attn_cols(q, k, v, dout, cols, scale=None, causal=False):
-    """One head: dK and dV for the listed key rows only."""
+def attn_cols(q, k, v, dout, cols, scale=None, causal=False, causal_offset=0):
+    """One head: dK and dV for the listed key rows only (causal mask as in
+    attn_rows)."""
     q, k, v, do = (_f64(t) for t in (q, k, v, dout))
     n, d = q.shape
     m, dv = v.shape
@@ -202,7 +207,55 @@ def attn_cols(q, k, v, dout, cols, scale=None, causal=False):
     dk = np.zeros((c, d)); dvv = np.zeros((c, dv))
     rc = _load().oracle_attn_cols(
         _ptr(q), _ptr(k), _ptr(v), _ptr(do), n, m, d, dv, float(scale), int(bool(causal)),
-        cols.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), c, _ptr(dk), _ptr(dvv))
+        int(causal_offset), cols.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), c, _ptr(dk),
+        _ptr(dvv))
     if rc:
         raise ValueError("oracle_attn_cols: invalid arguments")
     return {"dk": dk, "dv": dvv}
+
+
+MASKS = {"none": 0, "causal": 1, "causal_bottom_right": 2}
+
+
+def attn_bwd_masked(q, k, v, dout, scale=None, mask="none", seqlens_q=None, seqlens_k=None):
+    """Forward and backward with per-batch lengths and a mask mode.
+
+    ``mask``: "none", "causal" (key j visible from row i when j <= i) or
+    "causal_bottom_right" (j <= i + nk[b] - nq[b]).  ``seqlens_q`` and
+    ``seqlens_k`` (length B, or None for n and m) give the rows of each
+    batch element that take part; the rest is padding.  Rows that see no
+    key, and padded rows, get O = 0, LSE = -inf, D = 0, dQ = 0; padded keys
+    get dK = dV = 0.  Returns a dict with o, lse, D, dq, dk, dv as
+    [B,H,...] float64 arrays.
+    """
+    q, k, v, do = (_as4d(_f64(t)) for t in (q, k, v, dout))
+    B, H, n, m, d, dv = _dims(q, k, v)
+    if do.shape != (B, H, n, dv):
+        raise ValueError(f"dout shape {do.shape} != {(B, H, n, dv)}")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+
+    def lens(x):
+        if x is None:
+            return None
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.int64).reshape(-1))
+        if a.shape != (B,):
+            raise ValueError(f"sequence lengths need shape ({B},), got {a.shape}")
+        return a
+
+    lq, lk = lens(seqlens_q), lens(seqlens_k)
+    out = {
+        "dq": np.zeros((B, H, n, d)), "dk": np.zeros((B, H, m, d)),
+        "dv": np.zeros((B, H, m, dv)), "D": np.zeros((B, H, n)),
+        "o": np.zeros((B, H, n, dv)), "lse": np.zeros((B, H, n)),
+    }
+    lp = ctypes.POINTER(ctypes.c_long)
+    rc = _load().oracle_attn_bwd_masked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(out["dq"]), _ptr(out["dk"]),
+        _ptr(out["dv"]), _ptr(out["D"]), _ptr(out["o"]), _ptr(out["lse"]),
+        B, H, n, m, d, dv, float(scale), MASKS[mask],
+        lq.ctypes.data_as(lp) if lq is not None else None,
+        lk.ctypes.data_as(lp) if lk is not None else None)
+    if rc:
+        raise ValueError("oracle_attn_bwd_masked: invalid sizes or mask")
+    return out
