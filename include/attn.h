@@ -55,12 +55,24 @@ extern "C" {
 /* Element type of q, k, v, o, dout, dq, dk, dv_out.  lse is always float32. */
 enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 };
 
+/*
+ * Mask modes of attn_fwd_ex / attn_bwd_ex.  The pages define the causal mask
+ * for n == m only (mlgrind "Forward" and "Inputs"; eulerpad P8), where the
+ * two causal modes coincide; for n_b != m_b they are two readings.
+ */
+enum attn_mask {
+    ATTN_MASK_NONE = 0,                /* every key j < m_b is visible */
+    ATTN_MASK_CAUSAL = 1,              /* key j visible from row i when j <= i */
+    ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 2  /* j <= i + m_b - n_b: the last query row
+                                          sees the last key */
+};
+
 /* Return codes. */
 enum attn_status {
     ATTN_OK = 0,
     ATTN_EINVAL = 1,          /* null pointer, negative size, m < 1, d or dv < 1, non-finite scale */
-    ATTN_ECAUSAL_SHAPE = 2,   /* causal requested with n != m (mlgrind "Inputs") */
-    ATTN_EUNSUPPORTED = 3,    /* dtype or (d, dv) pair not built, or unknown flag bits */
+    ATTN_ECAUSAL_SHAPE = 2,   /* attn_fwd/attn_bwd: causal with n != m (mlgrind "Inputs") */
+    ATTN_EUNSUPPORTED = 3,    /* dtype, (d, dv) pair or mask not built, or unknown flag bits */
     ATTN_EWORKSPACE = 4,      /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
     ATTN_EHIP = 5             /* the HIP runtime refused a launch */
 };
@@ -88,6 +100,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, void* stream);
 
 /*
+ * Forward with per-batch lengths and a mask mode (enum attn_mask).
+ *
+ * seqlens_q and seqlens_k are device arrays of B int32 (4-byte aligned), or
+ * NULL for n and m in every batch element.  Batch element b uses query rows
+ * i < n_b = seqlens_q[b] and key rows j < m_b = seqlens_k[b] of its n and m
+ * rows; the rest is padding, never read.  Lengths outside [0, n] and
+ * [0, m] are clamped into them (the library cannot check device values
+ * without synchronising).  Padded query rows, and rows that see no key
+ * (m_b == 0, or i < n_b - m_b under ATTN_MASK_CAUSAL_BOTTOM_RIGHT), are
+ * written as o = 0 and lse = -inf.  No n == m requirement.  Otherwise as
+ * attn_fwd, which is attn_fwd_ex with NULL lengths and mask
+ * ATTN_MASK_CAUSAL or ATTN_MASK_NONE.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                const int* seqlens_q, const int* seqlens_k,
+                int B, int H, int n, int m, int d, int dv, float scale, int mask,
+                int dtype, void* stream);
+
+/*
  * Bytes of device workspace attn_bwd needs for these sizes (a multiple of
  * 256; zero for an empty problem).  Holds per-row D and rescaled LSE.
  */
@@ -105,6 +136,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv_out,
              int B, int H, int n, int m, int d, int dv, float scale, int causal,
              int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward with per-batch lengths and a mask mode, the counterpart of
+ * attn_fwd_ex (same lengths, mask, scale; lse from attn_fwd_ex).  Padded
+ * query rows and rows that see no key get dq = 0; padded key rows get
+ * dk = dv_out = 0.  Workspace size as for attn_bwd (attn_bwd_workspace_bytes
+ * with the same B, H, n, m, d, dv, dtype).  Otherwise as attn_bwd.
+ */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv_out,
+                const int* seqlens_q, const int* seqlens_k,
+                int B, int H, int n, int m, int d, int dv, float scale, int mask,
+                int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* attn_status_str(int status);

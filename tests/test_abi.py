@@ -146,3 +146,60 @@ def test_binding_constants_match_header():
     body = re.search(r"enum attn_dtype \{([^}]*)\}", text).group(1)
     vals = dict((k.strip(), int(v)) for k, v in (e.split("=") for e in body.split(",")))
     assert vals == {"ATTN_F32": B.ATTN_F32, "ATTN_BF16": B.ATTN_BF16, "ATTN_F16": B.ATTN_F16}
+
+
+def _fwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, dtype=B.ATTN_BF16,
+            sq=None, sk=None, ptrs=None):
+    p = ptrs if ptrs is not None else [FAKE] * 5
+    return lib.attn_fwd_ex(*p, sq, sk, B_, H, n, m, d, dv, scale, mask, dtype, NULL)
+
+
+def _bwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, dtype=B.ATTN_BF16,
+            flags=0, sq=None, sk=None, ws=FAKE, ws_bytes=1 << 30, ptrs=None):
+    p = ptrs if ptrs is not None else [FAKE] * 9
+    return lib.attn_bwd_ex(*p, sq, sk, B_, H, n, m, d, dv, scale, mask, dtype, flags, ws,
+                           ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=3), B.ATTN_EUNSUPPORTED),
+    (dict(mask=-1), B.ATTN_EUNSUPPORTED),
+    (dict(n=-1), B.ATTN_EINVAL),
+    (dict(m=0), B.ATTN_EINVAL),
+    (dict(scale=float("nan")), B.ATTN_EINVAL),
+    (dict(d=96, dv=96), B.ATTN_EUNSUPPORTED),
+    (dict(sq=ctypes.c_void_p((1 << 20) + 2)), B.ATTN_EINVAL),
+    (dict(sk=ctypes.c_void_p((1 << 20) + 1)), B.ATTN_EINVAL),
+])
+def test_ex_rejects(lib, kw, code):
+    assert _fwd_ex(lib, **kw) == code
+    assert _bwd_ex(lib, **kw) == code
+
+
+def test_ex_empty_problem_needs_no_pointers(lib):
+    # B*H == 0 with causal n != m: valid for the _ex entry points, nothing launched
+    assert _fwd_ex(lib, B_=0, n=3, m=70, mask=B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT,
+                   ptrs=[NULL] * 5) == B.ATTN_OK
+    assert _bwd_ex(lib, B_=0, n=3, m=70, mask=B.ATTN_MASK_CAUSAL, ptrs=[NULL] * 9, ws=NULL,
+                   ws_bytes=0) == B.ATTN_OK
+    # the plain entry points still reject causal n != m
+    assert _fwd(lib, B_=0, n=3, m=70, causal=1, ptrs=[NULL] * 5) == B.ATTN_ECAUSAL_SHAPE
+
+
+def test_binding_mask_arguments():
+    with pytest.raises(ValueError):
+        B._mask_code(True, "causal")
+    assert B._mask_code(False, None) == B.ATTN_MASK_NONE
+    assert B._mask_code(True, None) == B.ATTN_MASK_CAUSAL
+    assert B._mask_code(False, "causal_bottom_right") == B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT
+    with pytest.raises(KeyError):
+        B._mask_code(False, "sliding_window")
+
+
+def test_mask_constants_match_header():
+    text = open(HEADER).read()
+    body = re.search(r"enum attn_mask \{(.*?)\};", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    vals = dict((k.strip(), int(v)) for k, v in (e.split("=") for e in body.split(",") if "=" in e))
+    assert vals == {"ATTN_MASK_NONE": B.ATTN_MASK_NONE, "ATTN_MASK_CAUSAL": B.ATTN_MASK_CAUSAL,
+                    "ATTN_MASK_CAUSAL_BOTTOM_RIGHT": B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT}

@@ -21,12 +21,15 @@ ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
 ATTN_DQ_AUTO, ATTN_DQ_SEPARATE = 0, 1
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
+         "causal_bottom_right": ATTN_MASK_CAUSAL_BOTTOM_RIGHT}
 ATTN_STAGE_PREPROCESS, ATTN_STAGE_DKDV, ATTN_STAGE_DQ = 1 << 8, 1 << 9, 1 << 10
 DQ_MODES = {"auto": ATTN_DQ_AUTO, "separate": ATTN_DQ_SEPARATE}
 STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
 
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
-            "attn_version")
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
+            "attn_status_str", "attn_version")
 
 _lib = None
 
@@ -53,6 +56,10 @@ def load():
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_bwd.argtypes = [vp] * 9 + [I] * 6 + [F, I, I, I, vp, Z, vp]
     lib.attn_bwd.restype = I
+    lib.attn_fwd_ex.argtypes = [vp] * 7 + [I] * 6 + [F, I, I, vp]
+    lib.attn_fwd_ex.restype = I
+    lib.attn_bwd_ex.argtypes = [vp] * 11 + [I] * 6 + [F, I, I, I, vp, Z, vp]
+    lib.attn_bwd_ex.restype = I
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -98,8 +105,33 @@ def _shape(q, k, v):
     return B, H, n, m, d, dv
 
 
-def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
-    """O [B,H,n,dv] (q's dtype) and LSE [B,H,n] (float32, natural log)."""
+def _lens(t, B):
+    """A per-batch length tensor (int32 [B] on the GPU) or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or tuple(t.shape) != (B,):
+        raise ValueError(f"sequence lengths must be int32 of shape ({B},)")
+    _check_dev(t)
+    return t
+
+
+def _mask_code(causal, mask):
+    if mask is None:
+        return ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE
+    if causal:
+        raise ValueError("give either causal=True or mask=..., not both")
+    return MASKS[mask]
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, mask=None, seqlens_q=None,
+        seqlens_k=None):
+    """O [B,H,n,dv] (q's dtype) and LSE [B,H,n] (float32, natural log).
+
+    ``causal=True`` is the causal mask with n == m.  ``mask`` ("none",
+    "causal" or "causal_bottom_right") and the per-batch lengths
+    ``seqlens_q`` / ``seqlens_k`` (int32 [B] on the GPU) select the general
+    entry point, attn_fwd_ex.
+    """
     lib = load()
     _check_dev(q, k, v)
     B, H, n, m, d, dv = _shape(q, k, v)
@@ -110,10 +142,18 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
     if lse is None:
         lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
     _check_dev(out, lse)
-    st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n, m, d, dv,
-                      float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+    if mask is None and seqlens_q is None and seqlens_k is None:
+        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n, m, d, dv,
+                          float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+        where = "attn_fwd"
+    else:
+        code = _mask_code(causal, mask)
+        sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
+        st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sq), _ptr(sk),
+                             B, H, n, m, d, dv, float(scale), code, _dtype_code(q), _stream(q))
+        where = "attn_fwd_ex"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, where)
     return out, lse
 
 
@@ -125,11 +165,12 @@ def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto")
 
 
 def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace=None,
-        dq=None, dk=None, dv=None, stages=None):
+        dq=None, dk=None, dv=None, stages=None, mask=None, seqlens_q=None, seqlens_k=None):
     """(dq, dk, dv) with the shapes and dtype of (q, k, v).
 
     ``stages`` (a subset of {"preprocess", "dkdv", "dq"}) restricts which
-    kernels run; it exists for timing single kernels.
+    kernels run; it exists for timing single kernels.  ``mask`` and the
+    per-batch lengths select attn_bwd_ex, as in fwd().
     """
     lib = load()
     _check_dev(q, k, v, o, do, lse)
@@ -148,10 +189,20 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _check_dev(dq, dk, dv, workspace)
-    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                      _ptr(dk), _ptr(dv), B, H, n, m, d, dvw, float(scale), int(bool(causal)),
-                      code, flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                      _stream(q))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if mask is None and seqlens_q is None and seqlens_k is None:
+        st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, n, m, d, dvw, float(scale),
+                          int(bool(causal)), code, flags, _ptr(workspace), ws_bytes, _stream(q))
+        where = "attn_bwd"
+    else:
+        mcode = _mask_code(causal, mask)
+        sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
+        st = lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(sq), _ptr(sk), B, H, n, m, d, dvw,
+                             float(scale), mcode, code, flags, _ptr(workspace), ws_bytes,
+                             _stream(q))
+        where = "attn_bwd_ex"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, where)
     return dq, dk, dv

@@ -24,14 +24,18 @@ bool is_16bit(int dtype) { return dtype == ATTN_BF16 || dtype == ATTN_F16; }
 static_assert(ATTN_F32 == attn::kDtypeF32 && ATTN_BF16 == attn::kDtypeBF16 &&
                   ATTN_F16 == attn::kDtypeF16,
               "dtype codes of the C ABI and the kernels agree");
+static_assert(ATTN_MASK_NONE == attn::kMaskNone && ATTN_MASK_CAUSAL == attn::kMaskCausal &&
+                  ATTN_MASK_CAUSAL_BOTTOM_RIGHT == attn::kMaskCausalBottomRight,
+              "mask codes of the C ABI and the kernels agree");
 
-// Sizes, dtype, head widths, causal shape and scale; shared by fwd and bwd.
-int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int causal, int dtype,
+// Sizes, dtype, head widths, mask mode and scale; shared by fwd and bwd.
+int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int mask, int dtype,
                   Problem* out) {
     if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_EUNSUPPORTED;
+    if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+        return ATTN_EUNSUPPORTED;
     if (B < 0 || H < 0 || n < 0 || m < 1 || d < 1 || dv < 1) return ATTN_EINVAL;
     if (!isfinite(scale)) return ATTN_EINVAL;
-    if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
     if (n > kMaxSeq || m > kMaxSeq) return ATTN_EUNSUPPORTED;
     if (is_16bit(dtype)) {
         const bool ok = (d == 64 && dv == 64) || (d == 128 && dv == 128) || (d == 128 && dv == 64);
@@ -48,10 +52,14 @@ int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int ca
     out->d = d;
     out->dv = dv;
     out->scale = scale;
-    out->causal = causal != 0;
+    out->mask = mask;
+    out->causal = mask != ATTN_MASK_NONE;
     out->dtype = dtype;
     return ATTN_OK;
 }
+
+// Per-batch length arrays: NULL, or 4-byte aligned device memory.
+bool lens_ok(const int* p) { return p == nullptr || aligned(p, 4); }
 
 // A tensor with elements needs a non-null pointer aligned for the kernels'
 // vector accesses (16 bytes for 16-bit rows, 4 bytes for float32).
@@ -90,11 +98,15 @@ const char* attn_status_str(int status) {
     }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int n, int m, int d, int dv, float scale, int causal, int dtype, void* stream) {
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                const int* seqlens_q, const int* seqlens_k, int B, int H, int n, int m, int d,
+                int dv, float scale, int mask, int dtype, void* stream) {
     Problem p;
-    int st = check_problem(B, H, n, m, d, dv, scale, causal, dtype, &p);
+    int st = check_problem(B, H, n, m, d, dv, scale, mask, dtype, &p);
     if (st != ATTN_OK) return st;
+    if (!lens_ok(seqlens_q) || !lens_ok(seqlens_k)) return ATTN_EINVAL;
+    p.seqlens_q = seqlens_q;
+    p.seqlens_k = seqlens_k;
     const long hq = p.heads() * (long)n, hk = p.heads() * (long)m;
     if (!tensor_ok(q, hq * d, dtype) || !tensor_ok(k, hk * d, dtype) ||
         !tensor_ok(v, hk * dv, dtype) || !tensor_ok(o, hq * dv, dtype) ||
@@ -111,6 +123,17 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return hip_status();
 }
 
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int n, int m, int d, int dv, float scale, int causal, int dtype, void* stream) {
+    Problem p;
+    int st = check_problem(B, H, n, m, d, dv, scale, causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE,
+                           dtype, &p);
+    if (st != ATTN_OK) return st;
+    if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
+    return attn_fwd_ex(q, k, v, o, lse, nullptr, nullptr, B, H, n, m, d, dv, scale,
+                       causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE, dtype, stream);
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags) {
     (void)flags;
@@ -119,13 +142,17 @@ size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int d
     return workspace_bytes(p);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-             const float* lse, void* dq, void* dk, void* dv_out, int B, int H, int n, int m,
-             int d, int dv, float scale, int causal, int dtype, int flags, void* workspace,
-             size_t workspace_bytes_given, void* stream) {
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv_out, const int* seqlens_q,
+                const int* seqlens_k, int B, int H, int n, int m, int d, int dv, float scale,
+                int mask, int dtype, int flags, void* workspace, size_t workspace_bytes_given,
+                void* stream) {
     Problem p;
-    int st = check_problem(B, H, n, m, d, dv, scale, causal, dtype, &p);
+    int st = check_problem(B, H, n, m, d, dv, scale, mask, dtype, &p);
     if (st != ATTN_OK) return st;
+    if (!lens_ok(seqlens_q) || !lens_ok(seqlens_k)) return ATTN_EINVAL;
+    p.seqlens_q = seqlens_q;
+    p.seqlens_k = seqlens_k;
     if (flags & ~(kDqModeMask | kStageMask)) return ATTN_EUNSUPPORTED;
     const int dq_mode = flags & kDqModeMask;
     if (dq_mode != ATTN_DQ_AUTO && dq_mode != ATTN_DQ_SEPARATE) return ATTN_EUNSUPPORTED;
@@ -176,6 +203,20 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     return ATTN_OK;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv_out, int B, int H, int n, int m,
+             int d, int dv, float scale, int causal, int dtype, int flags, void* workspace,
+             size_t workspace_bytes_given, void* stream) {
+    Problem p;
+    int st = check_problem(B, H, n, m, d, dv, scale, causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE,
+                           dtype, &p);
+    if (st != ATTN_OK) return st;
+    if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
+    return attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv_out, nullptr, nullptr, B, H, n, m, d,
+                       dv, scale, causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE, dtype, flags,
+                       workspace, workspace_bytes_given, stream);
 }
 
 }  // extern "C"

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ Dw, T* __restrict__ dq, int n, int m, int n_pad, float scale,
-    float c2) {
+    float c2, SeqInfo si) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     // One LDS variable per buffer: the compiler can then tell that reads
@@ -63,6 +63,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const long bh = blockIdx.x;
     const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
     const int i0 = qb * C::BM;
+    // This head's query and key lengths and causal offset: rows i < nb take
+    // part, keys j < mb, and key j is visible from row i when j <= i + off.
+    const SeqLens len = seq_lens(si, bh, n, m);
+    const int nb = len.n, mb = len.m, off = len.off;
 
     const T* qh = q + bh * (long)n * D;
     const T* kh = k + bh * (long)m * D;
@@ -71,15 +75,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31).
     // Taking one tile from each half of the workgroup's rows gives every
-    // wave the same share of the masked diagonal work.  Rows past n load
-    // zeros and LSE2 = +inf, so their P, dS and dQ contributions vanish.
+    // wave the same share of the masked diagonal work.  Rows past nb load
+    // zeros and LSE2 = +inf, so their P, dS and dQ vanish.
     int myq[2];
     vec8<T> qreg[2][D / 16], oreg[2][DV / 16];
     float l2[2], Dq[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         myq[t] = i0 + (C::BM / 2) * t + 32 * wave + li;
-        const bool ok = myq[t] < n;
+        const bool ok = myq[t] < nb;
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc)
             qreg[t][kc] = ok ? gload8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : vec8<T>{};
@@ -101,18 +105,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     TileOffsets<DV> toV;
     toV.init(lane);
 
-    const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
-    const int nsteps = (k_end + BN - 1) / BN;
-    // Leading steps that need no mask: every key below the workgroup's
-    // first query (causal) and inside the m keys.  The rest are masked.
-    int n_plain = min(nsteps, m / BN);
-    if (CAUSAL) n_plain = min(n_plain, i0 / BN);
+    int k_end = CAUSAL ? min(mb, i0 + C::BM + off) : mb;
+    if (i0 >= nb) k_end = 0;
+    const int nsteps = (max(k_end, 0) + BN - 1) / BN;
+    // Leading steps that need no mask: keys visible from the workgroup's
+    // first query (causal) and inside the mb keys.  The rest are masked.
+    int n_plain = min(nsteps, mb / BN);
+    if (CAUSAL) n_plain = min(n_plain, max(i0 + off + 1, 0) / BN);
 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead.
-    // Rows past m (last tile only) come back as zeros; masked steps zero
+    // Rows past mb (last tile only) come back as zeros; masked steps zero
     // their P.
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)m * D * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)m * DV * 2);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * D * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * DV * 2);
     TileLoader<D, BN, NW> ldK;
     ldK.init(wave, lane);
     TileLoader<DV, BN, NW> ldV;
@@ -165,8 +170,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if constexpr (MASKED) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                lim[t] = m - 1 - k0 - 4 * g;
-                if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] - k0 - 4 * g);
+                lim[t] = mb - 1 - k0 - 4 * g;
+                if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] + off - k0 - 4 * g);
             }
         }
         // P for slot e of tile (kh, t), written over S; key k0 + 32kh + 4g +
@@ -296,14 +301,15 @@ void launch_dq(const Problem& p, const void* q, const void* k, const void* v, co
     using C = DqCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
+    const SeqInfo si = seq_info(p);
     if (p.causal)
         bwd_dq_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2, si);
     else
         bwd_dq_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2);
+            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2, si);
 }
 
 template <typename T>

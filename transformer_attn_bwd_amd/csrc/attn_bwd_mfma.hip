@@ -28,7 +28,8 @@ namespace {
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ lse2, float* __restrict__ Dw, int n, int n_pad, long total_rows) {
+    float* __restrict__ lse2, float* __restrict__ Dw, int n, int n_pad, long total_rows,
+    SeqInfo si) {
     constexpr int LPR = DV / 8;        // lanes per row, 8 elements (16 bytes) each
     constexpr int RPB = 256 / LPR;     // rows per block
     const int tid = threadIdx.x;
@@ -37,8 +38,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     const bool valid_row = row < total_rows;
     const long bh = valid_row ? row / n_pad : 0;
     const int i = valid_row ? (int)(row % n_pad) : 0;
+    const int nb = seq_lens(si, bh, n, 1).n;
     float acc = 0.f;
-    if (valid_row && i < n) {
+    if (valid_row && i < nb) {
         const long off = (bh * (long)n + i) * DV + 8 * part;
         vec8<T> a = gload8(o + off);
         vec8<T> b = gload8(dout + off);
@@ -47,8 +49,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    // Rows past nb, and rows that saw no key (LSE = -inf), get LSE2 = +inf
+    // so that every P of theirs is exactly 0.
     if (valid_row && part == 0) {
-        lse2[row] = i < n ? lse[bh * (long)n + i] * kLog2e : INFINITY;
+        const float l = i < nb ? lse[bh * (long)n + i] : -INFINITY;
+        lse2[row] = l > -INFINITY ? l * kLog2e : INFINITY;
         Dw[row] = acc;
     }
 }
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ Dw, T* __restrict__ dk, T* __restrict__ dvo, int n, int m,
-    int n_pad, float scale, float c2) {
+    int n_pad, float scale, float c2, SeqInfo si) {
     using C = DkdvCfg<D, DV>;
     using SC = DkdvSched<D, DV>;
     constexpr int BM = C::BM, NW = C::NW, LA = C::LA;
@@ -148,6 +153,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const long bh = blockIdx.x;
     const int j0 = blockIdx.y * C::BN;
     const int kw0 = j0 + C::KW * wave;      // this wave's first key
+    // This head's query and key lengths and causal offset: rows i < nb take
+    // part, keys j < mb, and key j is visible from row i when j <= i + off.
+    const SeqLens len = seq_lens(si, bh, n, m);
+    const int nb = len.n, mb = len.m, off = len.off;
 
     const T* qh = q + bh * (long)n * D;
     const T* kh = k + bh * (long)m * D;
@@ -156,12 +165,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const float* lh = lse2 + bh * (long)n_pad;
     const float* dh = Dw + bh * (long)n_pad;
 
-    // K rows j0 .. j0+255 into LDS (rows past m read as zeros: their S and
-    // P only reach dK and dV rows that are never written).
+    // K rows j0 .. j0+255 into LDS (rows past mb read as zeros: their S and
+    // P only reach dK and dV rows that are written as zeros).
     {
         TileLoader<D, C::BN, NW> ldK;
         ldK.init(wave, lane);
-        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)m * D * 2), j0, wave);
+        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)mb * D * 2), j0, wave);
     }
     // This lane's V row for key tile kt (key kw0 + 32 kt + li): B operand of
     // dP = dO V^T.
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int key = kw0 + 32 * kt + li;
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
-            vreg[kt][kc] = key < m ? gload8(vh + (long)key * DV + 16 * kc + 8 * g) : vec8<T>{};
+            vreg[kt][kc] = key < mb ? gload8(vh + (long)key * DV + 16 * kc + 8 * g) : vec8<T>{};
     }
 
     TileOffsets<D> toQ;
@@ -180,18 +189,25 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     toO.init(lane);
     const T* Kw = sK + C::KW * wave * D;  // this wave's 64 K rows
 
-    const int i_begin = CAUSAL ? j0 : 0;
-    const int i_end = (n + BM - 1) / BM * BM;
-    const int nsteps = i_end > i_begin ? (i_end - i_begin) / BM : 0;
-    // Causal: the query tiles below the workgroup's last key straddle the
-    // diagonal and are masked; the rest see every key of the workgroup.
-    const int n_masked = CAUSAL ? min(nsteps, C::BN / BM) : 0;
+    // Causal: rows below j0 - off see none of the workgroup's keys; query
+    // tiles that start below its last key minus off straddle the diagonal
+    // and are masked, the rest see every key of the workgroup.  The masked
+    // run is made even unless it covers every step, so that the plain loop
+    // starts on buffer 0.
+    const int i_begin = CAUSAL ? max(j0 - off, 0) / BM * BM : 0;
+    const int i_end = (nb + BM - 1) / BM * BM;
+    const int nsteps = (j0 < mb && i_end > i_begin) ? (i_end - i_begin) / BM : 0;
+    int n_masked = 0;
+    if (CAUSAL) {
+        n_masked = min(max((j0 + C::BN - 1 - off - i_begin + BM - 1) / BM, 0), nsteps);
+        if (n_masked < nsteps) n_masked = min((n_masked + 1) & ~1, nsteps);
+    }
 
-    // Query tile i0 into a buffer: Q and dO rows (rows past n come back as
+    // Query tile i0 into a buffer: Q and dO rows (rows past nb come back as
     // zeros; their LSE2 is +inf, so P = 0 and they contribute nothing), and
     // the per-row LSE2 and D.
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)n * D * 2);
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)n * DV * 2);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)nb * D * 2);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)nb * DV * 2);
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(lh, (uint32_t)n_pad * 4);
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(dh, (uint32_t)n_pad * 4);
     TileLoader<D, BM, NW> ldQ;
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // i.e. when 8(e>>2) + (e&3) < lim[kt].
         int lim[2];
         if constexpr (MASKED) {
-            lim[0] = kw0 + li - i0 - 4 * g;
+            lim[0] = kw0 + li - off - i0 - 4 * g;
             lim[1] = lim[0] + 32;
         }
 
@@ -369,7 +385,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // Accumulator slot vv of tile (kt, x) holds key kw0 + 32kt + 8(vv>>2) +
-    // 4g + (vv&3), column 32x + li.
+    // 4g + (vv&3), column 32x + li.  Keys past mb are padding: zeros.
     T* dkh = dk + bh * (long)m * D;
     T* dvh = dvo + bh * (long)m * DV;
 #pragma unroll
@@ -377,13 +393,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv) {
             const int key = kw0 + 32 * kt + 8 * (vv >> 2) + 4 * g + (vv & 3);
+            // (a padded key's accumulators may hold inf: S = 0 there, and P
+            // = exp2(-LSE2) overflows when a row's LSE is very negative, so
+            // its zeros are selected, not multiplied)
             if (key < m) {
+                const bool real = key < mb;
 #pragma unroll
                 for (int x = 0; x < D / 32; ++x)
-                    dkh[(long)key * D + 32 * x + li] = (T)(accK[kt][x][vv] * scale);
+                    dkh[(long)key * D + 32 * x + li] = real ? (T)(accK[kt][x][vv] * scale) : (T)0.f;
 #pragma unroll
                 for (int x = 0; x < DV / 32; ++x)
-                    dvh[(long)key * DV + 32 * x + li] = (T)accV[kt][x][vv];
+                    dvh[(long)key * DV + 32 * x + li] = real ? (T)accV[kt][x][vv] : (T)0.f;
             }
         }
     }
@@ -396,7 +416,8 @@ void launch_pre(const Problem& p, const void* o, const void* dout, const float* 
     const long total = p.heads() * (long)w.n_pad;
     const unsigned blocks = (unsigned)((total + RPB - 1) / RPB);
     bwd_preprocess_kernel<T, DV><<<blocks, 256, 0, s>>>((const T*)o, (const T*)dout, lse,
-                                                        w.lse2, w.D, p.n, w.n_pad, total);
+                                                        w.lse2, w.D, p.n, w.n_pad, total,
+                                                        seq_info(p));
 }
 
 template <typename T, int D, int DV>
@@ -405,14 +426,15 @@ void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
     using C = DkdvCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.m + C::BN - 1) / C::BN));
     const float c2 = p.scale * kLog2e;
+    const SeqInfo si = seq_info(p);
     if (p.causal)
         bwd_dkdv_kernel<T, D, DV, true><<<grid, 256, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2, si);
     else
         bwd_dkdv_kernel<T, D, DV, false><<<grid, 256, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2);
+            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2, si);
 }
 
 template <typename T>

@@ -3,8 +3,12 @@
 // This path exists for full-precision checks, not for speed: one wave per
 // row, lanes spread across the head dimension (two elements per lane at
 // most), dot products reduced across the wave.  The formulas are the same
-// as the bf16 path's (mlgrind "Forward"/"Backward"; eulerpad P2-P6), with
-// natural-base exponentials and float32 everywhere.
+// as the 16-bit path's (mlgrind "Forward"/"Backward"; eulerpad P2-P6), with
+// natural-base exponentials and float32 everywhere, and so are the
+// per-batch lengths and causal offsets: rows i < nb and keys j < mb take
+// part, key j is visible from row i when j <= i + off (causal), rows past
+// nb or with no visible key get O = 0, LSE = -inf, dQ = 0, keys past mb get
+// dK = dV = 0.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -52,11 +56,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ v,
                                                       float* __restrict__ o,
                                                       float* __restrict__ lse, int n, int m,
-                                                      int d, int dv, float scale, int causal) {
+                                                      int d, int dv, float scale, int causal,
+                                                      SeqInfo si) {
     const int lane = threadIdx.x & 63;
     const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
     const long bh = blockIdx.y;
     if (i >= n) return;
+    const SeqLens len = seq_lens(si, bh, n, m);
     const float* kh = k + bh * (long)m * d;
     const float* vh = v + bh * (long)m * dv;
     RowVec qi, acc;
@@ -64,7 +70,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < E; ++e) acc.x[e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
-    const int jend = causal ? i + 1 : m;
+    int jend = causal ? min(i + len.off + 1, len.m) : len.m;
+    if (i >= len.n) jend = 0;
     for (int j = 0; j < jend; ++j) {
         const float s = qi.dot(kh + (long)j * d, d, lane) * scale;
         const float m_new = fmaxf(m_run, s);
@@ -79,28 +86,31 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
         }
         m_run = m_new;
     }
-    acc.store(o + (bh * (long)n + i) * dv, dv, lane, 1.f / l_run);
-    if (lane == 0) lse[bh * (long)n + i] = m_run + logf(l_run);
+    const bool seen = jend > 0;
+    acc.store(o + (bh * (long)n + i) * dv, dv, lane, seen ? 1.f / l_run : 0.f);
+    if (lane == 0) lse[bh * (long)n + i] = seen ? m_run + logf(l_run) : -INFINITY;
 }
 
 // One thread per row: D_i = dO_i . O_i; LSE copied (natural base) into the
-// workspace; padded rows get zeros.
+// workspace.  Padded rows and rows that saw no key get LSE = +inf, so that
+// their P is exactly 0, and D = 0.
 __global__ __launch_bounds__(256) void preprocess_f32_kernel(
     const float* __restrict__ o, const float* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ lse_ws, float* __restrict__ Dw, int n, int n_pad, int dv,
-    long total_rows) {
+    long total_rows, SeqInfo si) {
     const long row = (long)blockIdx.x * 256 + threadIdx.x;
     if (row >= total_rows) return;
     const long bh = row / n_pad;
     const int i = (int)(row % n_pad);
-    float acc = 0.f, l = 0.f;
-    if (i < n) {
+    const int nb = seq_lens(si, bh, n, 1).n;
+    float acc = 0.f, l = -INFINITY;
+    if (i < nb) {
         const float* orow = o + (bh * (long)n + i) * dv;
         const float* drow = dout + (bh * (long)n + i) * dv;
         for (int c = 0; c < dv; ++c) acc += orow[c] * drow[c];
         l = lse[bh * (long)n + i];
     }
-    lse_ws[row] = l;
+    lse_ws[row] = l > -INFINITY ? l : INFINITY;
     Dw[row] = acc;
 }
 
@@ -109,11 +119,12 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dout, const float* __restrict__ lse_ws,
     const float* __restrict__ Dw, float* __restrict__ dk, float* __restrict__ dvo, int n, int m,
-    int d, int dv, int n_pad, float scale, int causal) {
+    int d, int dv, int n_pad, float scale, int causal, SeqInfo si) {
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
     const long bh = blockIdx.y;
     if (j >= m) return;
+    const SeqLens len = seq_lens(si, bh, n, m);
     const float* qh = q + bh * (long)n * d;
     const float* oh = dout + bh * (long)n * dv;
     RowVec kj, vj, gk, gv;
@@ -121,7 +132,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(
     vj.load(v + (bh * (long)m + j) * dv, dv, lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) gk.x[e] = gv.x[e] = 0.f;
-    for (int i = causal ? j : 0; i < n; ++i) {
+    const int iend = j < len.m ? len.n : 0;
+    for (int i = causal ? max(j - len.off, 0) : 0; i < iend; ++i) {
         const float* qi = qh + (long)i * d;
         const float* doi = oh + (long)i * dv;
         const float s = kj.dot(qi, d, lane) * scale;
@@ -144,11 +156,12 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dout, const float* __restrict__ lse_ws,
     const float* __restrict__ Dw, float* __restrict__ dq, int n, int m, int d, int dv, int n_pad,
-    float scale, int causal) {
+    float scale, int causal, SeqInfo si) {
     const int lane = threadIdx.x & 63;
     const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
     const long bh = blockIdx.y;
     if (i >= n) return;
+    const SeqLens len = seq_lens(si, bh, n, m);
     const float* kh = k + bh * (long)m * d;
     const float* vh = v + bh * (long)m * dv;
     RowVec qi, doi, g;
@@ -158,7 +171,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(
     for (int e = 0; e < E; ++e) g.x[e] = 0.f;
     const float li = lse_ws[bh * (long)n_pad + i];
     const float Di = Dw[bh * (long)n_pad + i];
-    const int jend = causal ? i + 1 : m;
+    int jend = causal ? min(i + len.off + 1, len.m) : len.m;
+    if (i >= len.n || li == INFINITY) jend = 0;
     for (int j = 0; j < jend; ++j) {
         const float* kj = kh + (long)j * d;
         const float s = qi.dot(kj, d, lane) * scale;
@@ -181,7 +195,7 @@ bool launch_fwd_f32(const Problem& p, const float* q, const float* k, const floa
     if (p.d > 64 * E || p.dv > 64 * E) return false;
     dim3 grid((unsigned)((p.n + 3) / 4), (unsigned)p.heads());
     fwd_f32_kernel<<<grid, 256, 0, s>>>(q, k, v, o, lse, p.n, p.m, p.d, p.dv, p.scale,
-                                        p.causal ? 1 : 0);
+                                        p.causal ? 1 : 0, seq_info(p));
     return true;
 }
 
@@ -189,7 +203,7 @@ bool launch_bwd_preprocess_f32(const Problem& p, const float* o, const float* do
                                const float* lse, const Workspace& w, hipStream_t s) {
     const long total = p.heads() * (long)w.n_pad;
     preprocess_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
-        o, dout, lse, w.lse2, w.D, p.n, w.n_pad, p.dv, total);
+        o, dout, lse, w.lse2, w.D, p.n, w.n_pad, p.dv, total, seq_info(p));
     return true;
 }
 
@@ -199,7 +213,7 @@ bool launch_bwd_dkdv_f32(const Problem& p, const float* q, const float* k, const
     if (p.d > 64 * E || p.dv > 64 * E) return false;
     dim3 grid((unsigned)((p.m + 3) / 4), (unsigned)p.heads());
     dkdv_f32_kernel<<<grid, 256, 0, s>>>(q, k, v, dout, w.lse2, w.D, dk, dv, p.n, p.m, p.d,
-                                         p.dv, w.n_pad, p.scale, p.causal ? 1 : 0);
+                                         p.dv, w.n_pad, p.scale, p.causal ? 1 : 0, seq_info(p));
     return true;
 }
 
@@ -208,7 +222,7 @@ bool launch_bwd_dq_f32(const Problem& p, const float* q, const float* k, const f
     if (p.d > 64 * E || p.dv > 64 * E) return false;
     dim3 grid((unsigned)((p.n + 3) / 4), (unsigned)p.heads());
     dq_f32_kernel<<<grid, 256, 0, s>>>(q, k, v, dout, w.lse2, w.D, dq, p.n, p.m, p.d, p.dv,
-                                       w.n_pad, p.scale, p.causal ? 1 : 0);
+                                       w.n_pad, p.scale, p.causal ? 1 : 0, seq_info(p));
     return true;
 }
 

@@ -38,7 +38,7 @@ constexpr float kRescaleThreshold = 8.f;     // log2 of the largest P allowed
 template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    T* __restrict__ o, float* __restrict__ lse, int n, int m, float c2) {
+    T* __restrict__ o, float* __restrict__ lse, int n, int m, float c2, SeqInfo si) {
     using C = FwdCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     constexpr int KA = D / 16, NXV = DV / 32;
@@ -58,6 +58,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const long bh = blockIdx.x;
     const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
     const int i0 = qb * C::BM;
+    // This head's query and key lengths and causal offset: rows i < nb take
+    // part, keys j < mb, and key j is visible from row i when j <= i + off.
+    const SeqLens len = seq_lens(si, bh, n, m);
+    const int nb = len.n, mb = len.m, off = len.off;
 
     const T* qh = q + bh * (long)n * D;
     const T* kh = k + bh * (long)m * D;
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         myq[t] = i0 + (C::BM / 2) * t + 32 * wave + li;
-        const bool ok = myq[t] < n;
+        const bool ok = myq[t] < nb;
 #pragma unroll
         for (int kc = 0; kc < KA; ++kc) {
             vec8<T> x = ok ? gload8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : vec8<T>{};
@@ -92,15 +96,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     TileOffsets<DV> toV;
     toV.init(lane);
 
-    const int k_end = CAUSAL ? min(m, i0 + C::BM) : m;
-    const int nsteps = (k_end + BN - 1) / BN;
-    int n_plain = min(nsteps, m / BN);
-    if (CAUSAL) n_plain = min(n_plain, i0 / BN);
+    // Keys below k_end reach some row of the workgroup; the first n_plain
+    // steps are visible from all of its rows and need no mask.
+    int k_end = CAUSAL ? min(mb, i0 + C::BM + off) : mb;
+    if (i0 >= nb) k_end = 0;
+    const int nsteps = (max(k_end, 0) + BN - 1) / BN;
+    int n_plain = min(nsteps, mb / BN);
+    if (CAUSAL) n_plain = min(n_plain, max(i0 + off + 1, 0) / BN);
 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead;
-    // rows past m come back as zeros and are masked.
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)m * D * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)m * DV * 2);
+    // rows past mb come back as zeros and are masked.
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * D * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * DV * 2);
     TileLoader<D, BN, NW> ldK;
     ldK.init(wave, lane);
     TileLoader<DV, BN, NW> ldV;
@@ -146,13 +153,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
         f32x16 S[NKH][2];
         vec8<T> Pb[NC][2];
-        float mb[2];
+        float mbase[2];   // running max used as the exponent base
         int lim[2];
         if constexpr (MASKED) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                lim[t] = m - 1 - k0 - 4 * g;
-                if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] - k0 - 4 * g);
+                lim[t] = mb - 1 - k0 - 4 * g;
+                if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] + off - k0 - 4 * g);
             }
         }
         auto visible = [&](int kh, int e, int t) __attribute__((always_inline)) {
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 }
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t) mb[t] = m_run[t] == -INFINITY ? 0.f : m_run[t];
+            for (int t = 0; t < 2; ++t) mbase[t] = m_run[t] == -INFINITY ? 0.f : m_run[t];
         };
         auto p_chunk = [&](auto c_, auto t_) __attribute__((always_inline)) {
             constexpr int c = decltype(c_)::value, t = decltype(t_)::value;
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             float p8[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                float pv = fast_exp2(__builtin_fmaf(S[kh][t][e0 + s], cs, -mb[t]));
+                float pv = fast_exp2(__builtin_fmaf(S[kh][t][e0 + s], cs, -mbase[t]));
                 if constexpr (MASKED) pv = visible(kh, e0 + s, t) ? pv : 0.f;
                 p8[s] = pv;
                 l_run[t] += pv;
@@ -277,11 +284,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Accumulator slot vv of tile (x, t) holds column 32x + 8(vv>>2) + 4g +
     // (vv&3) of query myq[t]; the row sum is split over this lane and the
-    // lane 32 away.
+    // lane 32 away.  Rows past nb, and rows that see no key (row sum 0),
+    // are written as O = 0, LSE = -inf.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float l_tot = l_run[t] + xor_lane32(l_run[t]);
-        const float inv = 1.f / l_tot;
+        const bool seen = myq[t] < nb && l_tot > 0.f;
+        const float inv = seen ? 1.f / l_tot : 0.f;
         if (myq[t] < n) {
             T* orow = o + (bh * (long)n + myq[t]) * DV;
 #pragma unroll
@@ -294,7 +303,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     *reinterpret_cast<vec4<T>*>(orow + 32 * x + 8 * vq + 4 * g) = w;
                 }
             }
-            if (g == 0) lse[bh * (long)n + myq[t]] = (m_run[t] + log2f(l_tot)) * kLn2;
+            if (g == 0)
+                lse[bh * (long)n + myq[t]] = seen ? (m_run[t] + log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
 }
@@ -305,12 +315,13 @@ void launch(const Problem& p, const void* q, const void* k, const void* v, void*
     using C = FwdCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
+    const SeqInfo si = seq_info(p);
     if (p.causal)
         fwd_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
-            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2);
+            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2, si);
     else
         fwd_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
-            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2);
+            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2, si);
 }
 
 template <typename T>

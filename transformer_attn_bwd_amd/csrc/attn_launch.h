@@ -11,14 +11,48 @@ constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 constexpr int kDtypeF16 = 2;
 
+// Mask modes, the values of enum attn_mask in attn.h.
+constexpr int kMaskNone = 0;
+constexpr int kMaskCausal = 1;              // key j visible from row i when j <= i
+constexpr int kMaskCausalBottomRight = 2;   // j <= i + m_b - n_b
+
 struct Problem {
     long B = 0, H = 0;
     int n = 0, m = 0, d = 0, dv = 0;
     float scale = 1.f;
-    bool causal = false;
+    bool causal = false;                    // mask != kMaskNone
+    int mask = kMaskNone;
     int dtype = 0;
+    const int* seqlens_q = nullptr;         // device [B] or null (n for every b)
+    const int* seqlens_k = nullptr;         // device [B] or null (m for every b)
     long heads() const { return B * H; }
 };
+
+// What the kernels need to find a head's lengths and causal offset.
+struct SeqInfo {
+    const int* sq;     // per-batch query lengths or null
+    const int* sk;     // per-batch key lengths or null
+    int H;             // heads per batch element (blockIdx.x / H is the batch)
+    int br;            // 1: causal diagonal aligned bottom-right
+};
+
+inline SeqInfo seq_info(const Problem& p) {
+    return {p.seqlens_q, p.seqlens_k, (int)p.H, p.mask == kMaskCausalBottomRight ? 1 : 0};
+}
+
+// Lengths of head bh: n_b query rows and m_b key rows take part (values
+// clamped into [0, n] and [0, m]); under the causal mask key j is visible
+// from row i when j <= i + off.
+struct SeqLens {
+    int n, m, off;
+};
+__device__ __forceinline__ SeqLens seq_lens(const SeqInfo& si, long bh, int n, int m) {
+    const int b = (int)bh / si.H;
+    int nb = n, mb = m;
+    if (si.sq) nb = min(max(si.sq[b], 0), n);
+    if (si.sk) mb = min(max(si.sk[b], 0), m);
+    return {nb, mb, si.br ? mb - nb : 0};
+}
 
 // Rows per head in the backward workspace (per-row D and rescaled LSE),
 // padded so that every query tile the kernels touch is in bounds.
