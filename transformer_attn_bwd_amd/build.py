@@ -17,8 +17,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_api.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip",
-           "attn_f32.hip"]
+# (source, element type or None): the MFMA kernel files are compiled once per
+# 16-bit element type, so that the slow instantiations build in parallel.
+ELEMS = ("bf16", "f16")
+MFMA_SOURCES = ["attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip"]
+SOURCES = ["attn_api.hip", "attn_f32.hip", *MFMA_SOURCES]
+UNITS = [("attn_api.hip", None), ("attn_f32.hip", None)] + [
+    (src, elem) for src in MFMA_SOURCES for elem in ELEMS]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -39,9 +44,12 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit: tuple[str, str | None], extra: list[str]) -> str:
+    src, elem = unit
+    stem = os.path.splitext(src)[0] + (f"_{elem}" if elem else "")
+    obj = os.path.join(OBJ_DIR, stem + ".o")
+    defs = [f"-DATTN_ELEM={elem}"] if elem else []
+    cmd = [hipcc(), *COMMON_FLAGS, *defs, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -52,8 +60,9 @@ def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
     """Compile every source and link libattn.so; returns its path."""
     extra = list(extra_flags or [])
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 5)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+    workers = max(1, min(len(UNITS), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda u: _compile(u, extra), UNITS))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

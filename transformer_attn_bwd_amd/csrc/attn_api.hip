@@ -116,7 +116,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     bool ok = is_16bit(dtype)
-                  ? attn::launch_fwd_mfma(p, q, k, v, o, lse, s)
+                  ? (dtype == ATTN_BF16 ? attn::launch_fwd_mfma<__bf16>(p, q, k, v, o, lse, s)
+                                        : attn::launch_fwd_mfma<_Float16>(p, q, k, v, o, lse, s))
                   : attn::launch_fwd_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                          (float*)o, lse, s);
     if (!ok) return ATTN_EUNSUPPORTED;
@@ -182,21 +183,27 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     const bool bf = is_16bit(dtype);
     bool ok = true;
     if (n > 0 && (stages & ATTN_STAGE_PREPROCESS)) {
-        ok = bf ? attn::launch_bwd_preprocess_mfma(p, o, dout, lse, w, s)
+        ok = bf ? (dtype == ATTN_BF16
+                       ? attn::launch_bwd_preprocess_mfma<__bf16>(p, o, dout, lse, w, s)
+                       : attn::launch_bwd_preprocess_mfma<_Float16>(p, o, dout, lse, w, s))
                 : attn::launch_bwd_preprocess_f32(p, (const float*)o, (const float*)dout, lse, w, s);
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     if (stages & ATTN_STAGE_DKDV) {
         // With n == 0 the kernel visits no query tile and writes zeros.
-        ok = bf ? attn::launch_bwd_dkdv_mfma(p, q, k, v, dout, w, dk, dv_out, s)
+        ok = bf ? (dtype == ATTN_BF16
+                       ? attn::launch_bwd_dkdv_mfma<__bf16>(p, q, k, v, dout, w, dk, dv_out, s)
+                       : attn::launch_bwd_dkdv_mfma<_Float16>(p, q, k, v, dout, w, dk, dv_out, s))
                 : attn::launch_bwd_dkdv_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                             (const float*)dout, w, (float*)dk, (float*)dv_out, s);
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     if (n > 0 && (stages & ATTN_STAGE_DQ)) {
-        ok = bf ? attn::launch_bwd_dq_mfma(p, q, k, v, dout, w, dq, s)
+        ok = bf ? (dtype == ATTN_BF16
+                       ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, w, dq, s)
+                       : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, w, dq, s))
                 : attn::launch_bwd_dq_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                           (const float*)dout, w, (float*)dq, s);
         if (!ok) return ATTN_EUNSUPPORTED;

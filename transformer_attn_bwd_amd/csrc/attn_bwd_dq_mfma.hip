@@ -312,9 +312,11 @@ void launch_dq(const Problem& p, const void* q, const void* k, const void* v, co
             (T*)dq, p.n, p.m, w.n_pad, p.scale, c2, si);
 }
 
+}  // namespace
+
 template <typename T>
-bool dq_for_widths(const Problem& p, const void* q, const void* k, const void* v,
-                   const void* dout, const Workspace& w, void* dq, hipStream_t s) {
+bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
+                        const void* dout, const Workspace& w, void* dq, hipStream_t s) {
     if (p.d == 64 && p.dv == 64) launch_dq<T, 64, 64>(p, q, k, v, dout, w, dq, s);
     else if (p.d == 128 && p.dv == 128) launch_dq<T, 128, 128>(p, q, k, v, dout, w, dq, s);
     else if (p.d == 128 && p.dv == 64) launch_dq<T, 128, 64>(p, q, k, v, dout, w, dq, s);
@@ -322,13 +324,13 @@ bool dq_for_widths(const Problem& p, const void* q, const void* k, const void* v
     return true;
 }
 
-}  // namespace
-
-bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
-                        const void* dout, const Workspace& w, void* dq, hipStream_t s) {
-    if (p.dtype == kDtypeBF16) return dq_for_widths<bf16>(p, q, k, v, dout, w, dq, s);
-    if (p.dtype == kDtypeF16) return dq_for_widths<f16>(p, q, k, v, dout, w, dq, s);
-    return false;
-}
+// Each element type is compiled as its own object (-DATTN_ELEM=bf16 or f16)
+// so that the builds of the two instantiations run in parallel.
+#ifndef ATTN_ELEM
+#error "compile once per element type: -DATTN_ELEM=bf16 or -DATTN_ELEM=f16"
+#endif
+template bool launch_bwd_dq_mfma<ATTN_ELEM>(const Problem&, const void*, const void*,
+                                           const void*, const void*, const Workspace&, void*,
+                                           hipStream_t);
 
 }  // namespace attn

@@ -437,9 +437,21 @@ void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
             (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2, si);
 }
 
+}  // namespace
+
 template <typename T>
-bool dkdv_for_widths(const Problem& p, const void* q, const void* k, const void* v,
-                     const void* dout, const Workspace& w, void* dk, void* dv, hipStream_t s) {
+bool launch_bwd_preprocess_mfma(const Problem& p, const void* o, const void* dout,
+                                const float* lse, const Workspace& w, hipStream_t s) {
+    if (p.dv == 64) launch_pre<T, 64>(p, o, dout, lse, w, s);
+    else if (p.dv == 128) launch_pre<T, 128>(p, o, dout, lse, w, s);
+    else return false;
+    return true;
+}
+
+template <typename T>
+bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
+                          const void* dout, const Workspace& w, void* dk, void* dv,
+                          hipStream_t s) {
     if (p.d == 64 && p.dv == 64) launch_dkdv<T, 64, 64>(p, q, k, v, dout, w, dk, dv, s);
     else if (p.d == 128 && p.dv == 128) launch_dkdv<T, 128, 128>(p, q, k, v, dout, w, dk, dv, s);
     else if (p.d == 128 && p.dv == 64) launch_dkdv<T, 128, 64>(p, q, k, v, dout, w, dk, dv, s);
@@ -447,30 +459,15 @@ bool dkdv_for_widths(const Problem& p, const void* q, const void* k, const void*
     return true;
 }
 
-template <typename T>
-bool pre_for_widths(const Problem& p, const void* o, const void* dout, const float* lse,
-                    const Workspace& w, hipStream_t s) {
-    if (p.dv == 64) launch_pre<T, 64>(p, o, dout, lse, w, s);
-    else if (p.dv == 128) launch_pre<T, 128>(p, o, dout, lse, w, s);
-    else return false;
-    return true;
-}
-
-}  // namespace
-
-bool launch_bwd_preprocess_mfma(const Problem& p, const void* o, const void* dout,
-                                const float* lse, const Workspace& w, hipStream_t s) {
-    if (p.dtype == kDtypeBF16) return pre_for_widths<bf16>(p, o, dout, lse, w, s);
-    if (p.dtype == kDtypeF16) return pre_for_widths<f16>(p, o, dout, lse, w, s);
-    return false;
-}
-
-bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
-                          const void* dout, const Workspace& w, void* dk, void* dv,
-                          hipStream_t s) {
-    if (p.dtype == kDtypeBF16) return dkdv_for_widths<bf16>(p, q, k, v, dout, w, dk, dv, s);
-    if (p.dtype == kDtypeF16) return dkdv_for_widths<f16>(p, q, k, v, dout, w, dk, dv, s);
-    return false;
-}
+// Each element type is compiled as its own object (-DATTN_ELEM=bf16 or f16)
+// so that the builds of the two instantiations run in parallel.
+#ifndef ATTN_ELEM
+#error "compile once per element type: -DATTN_ELEM=bf16 or -DATTN_ELEM=f16"
+#endif
+template bool launch_bwd_preprocess_mfma<ATTN_ELEM>(const Problem&, const void*, const void*,
+                                                   const float*, const Workspace&, hipStream_t);
+template bool launch_bwd_dkdv_mfma<ATTN_ELEM>(const Problem&, const void*, const void*,
+                                             const void*, const void*, const Workspace&, void*,
+                                             void*, hipStream_t);
 
 }  // namespace attn

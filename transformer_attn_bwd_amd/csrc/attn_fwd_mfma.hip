@@ -324,9 +324,11 @@ void launch(const Problem& p, const void* q, const void* k, const void* v, void*
             (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2, si);
 }
 
+}  // namespace
+
 template <typename T>
-bool fwd_for_widths(const Problem& p, const void* q, const void* k, const void* v, void* o,
-                    float* lse, hipStream_t s) {
+bool launch_fwd_mfma(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                     float* lse, hipStream_t s) {
     if (p.d == 64 && p.dv == 64) launch<T, 64, 64>(p, q, k, v, o, lse, s);
     else if (p.d == 128 && p.dv == 128) launch<T, 128, 128>(p, q, k, v, o, lse, s);
     else if (p.d == 128 && p.dv == 64) launch<T, 128, 64>(p, q, k, v, o, lse, s);
@@ -334,13 +336,12 @@ bool fwd_for_widths(const Problem& p, const void* q, const void* k, const void* 
     return true;
 }
 
-}  // namespace
-
-bool launch_fwd_mfma(const Problem& p, const void* q, const void* k, const void* v, void* o,
-                     float* lse, hipStream_t s) {
-    if (p.dtype == kDtypeBF16) return fwd_for_widths<bf16>(p, q, k, v, o, lse, s);
-    if (p.dtype == kDtypeF16) return fwd_for_widths<f16>(p, q, k, v, o, lse, s);
-    return false;
-}
+// Each element type is compiled as its own object (-DATTN_ELEM=bf16 or f16)
+// so that the builds of the two instantiations run in parallel.
+#ifndef ATTN_ELEM
+#error "compile once per element type: -DATTN_ELEM=bf16 or -DATTN_ELEM=f16"
+#endif
+template bool launch_fwd_mfma<ATTN_ELEM>(const Problem&, const void*, const void*, const void*,
+                                        void*, float*, hipStream_t);
 
 }  // namespace attn

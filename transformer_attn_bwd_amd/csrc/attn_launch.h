@@ -66,15 +66,19 @@ struct Workspace {
     int n_pad;
 };
 
-// 16-bit MFMA path (p.dtype kDtypeBF16 or kDtypeF16); return false if
-// (d, dv) or the dtype has no instantiation.
+// 16-bit MFMA path, T = __bf16 or _Float16 (instantiated in the kernel
+// files); return false if (d, dv) has no instantiation.
+template <typename T>
 bool launch_fwd_mfma(const Problem& p, const void* q, const void* k, const void* v, void* o,
                      float* lse, hipStream_t s);
+template <typename T>
 bool launch_bwd_preprocess_mfma(const Problem& p, const void* o, const void* dout,
                                 const float* lse, const Workspace& w, hipStream_t s);
+template <typename T>
 bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
                           const void* dout, const Workspace& w, void* dk, void* dv,
                           hipStream_t s);
+template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const Workspace& w, void* dq, hipStream_t s);
 
