@@ -30,8 +30,9 @@
  *    either 16-bit type the products run on 16-bit matrix instructions
  *    with float32 accumulation; softmax statistics, LSE and D are float32,
  *    and P and dS are rounded to the input type before their products.
- *  - Supported (d, dv): ATTN_BF16 and ATTN_F16 {(64,64), (128,128), (128,64)};
- *    ATTN_F32 any d, dv in 1..128.
+ *  - Supported (d, dv): ATTN_BF16 and ATTN_F16 any multiples of 8 in 8..128
+ *    (each is padded with zero columns to 64 or 128 inside the kernels, so
+ *    64 and 128 waste no work); ATTN_F32 any d, dv in 1..128.
  *  - The caller owns every buffer.  The library allocates and frees nothing
  *    and never synchronises: work is enqueued on `stream` (a hipStream_t;
  *    NULL is the default stream) and the call returns.

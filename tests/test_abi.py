@@ -46,10 +46,11 @@ def test_workspace_size(lib):
     assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64) == 2 * 128 * 4
     assert attn.bwd_workspace_bytes(1, 1, 0, 5, 64, 64) == 0
     assert attn.bwd_workspace_bytes(0, 4, 100, 5, 64, 64) == 0
-    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 96, 96, B.ATTN_BF16, 0) == 0  # unsupported
+    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 100, 100, B.ATTN_BF16, 0) == 0  # unsupported
     for code in (B.ATTN_BF16, B.ATTN_F16, B.ATTN_F32):
         assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, 0) == 2 * 6 * 384 * 4
-    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 64, 128, B.ATTN_F16, 0) == 0  # unsupported
+    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 64, 136, B.ATTN_F16, 0) == 0  # unsupported
+    assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 96, 40, B.ATTN_F16, 0) > 0
 
 
 NULL = None
@@ -76,11 +77,12 @@ def _bwd(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, causal=0, dtype=B
     (dict(scale=float("nan")), B.ATTN_EINVAL),
     (dict(scale=float("inf")), B.ATTN_EINVAL),
     (dict(n=64, m=65, causal=1), B.ATTN_ECAUSAL_SHAPE),
-    (dict(d=96, dv=96), B.ATTN_EUNSUPPORTED),
-    (dict(d=64, dv=128), B.ATTN_EUNSUPPORTED),
+    (dict(d=100, dv=100), B.ATTN_EUNSUPPORTED),    # 16-bit widths: multiples of 8
+    (dict(d=64, dv=136), B.ATTN_EUNSUPPORTED),     # ... up to 128
+    (dict(d=4, dv=64), B.ATTN_EUNSUPPORTED),
     (dict(dtype=7), B.ATTN_EUNSUPPORTED),
-    (dict(dtype=B.ATTN_F16, d=96, dv=96), B.ATTN_EUNSUPPORTED),
-    (dict(dtype=B.ATTN_F16, d=64, dv=128), B.ATTN_EUNSUPPORTED),
+    (dict(dtype=B.ATTN_F16, d=100, dv=96), B.ATTN_EUNSUPPORTED),
+    (dict(dtype=B.ATTN_F16, d=256, dv=128), B.ATTN_EUNSUPPORTED),
     (dict(dtype=B.ATTN_F32, d=129), B.ATTN_EUNSUPPORTED),
     (dict(n=(1 << 22) + 1, m=(1 << 22) + 1), B.ATTN_EUNSUPPORTED),
 ])
@@ -167,7 +169,7 @@ def _bwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, dtype=
     (dict(n=-1), B.ATTN_EINVAL),
     (dict(m=0), B.ATTN_EINVAL),
     (dict(scale=float("nan")), B.ATTN_EINVAL),
-    (dict(d=96, dv=96), B.ATTN_EUNSUPPORTED),
+    (dict(d=100, dv=96), B.ATTN_EUNSUPPORTED),
     (dict(sq=ctypes.c_void_p((1 << 20) + 2)), B.ATTN_EINVAL),
     (dict(sk=ctypes.c_void_p((1 << 20) + 1)), B.ATTN_EINVAL),
 ])

@@ -97,6 +97,29 @@ def test_fp16_shapes(w):
     compare_full(w, run_gpu(w, inputs), oracle_full(w, inputs))
 
 
+WIDTH_SHAPES = [
+    # head widths other than 64 and 128 (multiples of 8 up to 128): the
+    # kernels pad them with zero columns to 64- or 128-wide tiles
+    _w("bf16_d32_causal", 1, 2, 300, 300, 32, 32, "bf16", True, 61),
+    _w("bf16_d96_cross", 1, 2, 200, 333, 96, 96, "bf16", False, 62),
+    _w("bf16_d80_causal", 2, 1, 257, 257, 80, 80, "bf16", True, 63),
+    _w("bf16_d64_dv128", 1, 2, 300, 300, 64, 128, "bf16", True, 64),
+    _w("bf16_d8_dv8", 1, 1, 130, 70, 8, 8, "bf16", False, 65),
+    _w("bf16_d128_dv32", 1, 2, 190, 190, 128, 32, "bf16", True, 66),
+    _w("bf16_d40_dv72", 1, 1, 100, 520, 40, 72, "bf16", False, 67),
+    _w("bf16_d112_dv120", 1, 1, 333, 333, 112, 120, "bf16", True, 68),
+    _w("f16_d96_causal", 1, 2, 400, 400, 96, 96, "fp16", True, 69),
+    _w("f16_d48_dv128", 1, 1, 150, 300, 48, 128, "fp16", False, 70, 3.0),
+]
+
+
+@pytest.mark.parametrize("w", WIDTH_SHAPES, ids=lambda w: w.name)
+def test_head_widths(w):
+    say(f"case {w.describe()}")
+    inputs = make_inputs(w)
+    compare_full(w, run_gpu(w, inputs), oracle_full(w, inputs))
+
+
 def test_fp16_and_bf16_agree_on_exact_inputs():
     """Inputs that both 16-bit types hold exactly (small integers times
     powers of two) give the two instantiations the same problem; their

@@ -38,7 +38,8 @@ int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int ma
     if (!isfinite(scale)) return ATTN_EINVAL;
     if (n > kMaxSeq || m > kMaxSeq) return ATTN_EUNSUPPORTED;
     if (is_16bit(dtype)) {
-        const bool ok = (d == 64 && dv == 64) || (d == 128 && dv == 128) || (d == 128 && dv == 64);
+        // head widths padded to 64 or 128 columns inside the kernels
+        const bool ok = d <= 128 && dv <= 128 && d % 8 == 0 && dv % 8 == 0;
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((long)B * H > 0x7fffffffL) return ATTN_EUNSUPPORTED;
     } else {

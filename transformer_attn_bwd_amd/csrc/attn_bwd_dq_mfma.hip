@@ -38,8 +38,8 @@ template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ Dw, T* __restrict__ dq, int n, int m, int n_pad, float scale,
-    float c2, SeqInfo si) {
+    const float* __restrict__ Dw, T* __restrict__ dq, int n, int m, int dg, int dvg, int n_pad,
+    float scale, float c2, SeqInfo si) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     // One LDS variable per buffer: the compiler can then tell that reads
@@ -68,10 +68,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const SeqLens len = seq_lens(si, bh, n, m);
     const int nb = len.n, mb = len.m, off = len.off;
 
-    const T* qh = q + bh * (long)n * D;
-    const T* kh = k + bh * (long)m * D;
-    const T* vh = v + bh * (long)m * DV;
-    const T* oh = dout + bh * (long)n * DV;
+    // Rows of Q and K hold dg <= D elements, rows of V and dO dvg <= DV (each
+    // a multiple of 8); the columns past them are zeros in registers and
+    // LDS, so they add nothing to any product.
+    const T* qh = q + bh * (long)n * dg;
+    const T* kh = k + bh * (long)m * dg;
+    const T* vh = v + bh * (long)m * dvg;
+    const T* oh = dout + bh * (long)n * dvg;
 
     // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31).
     // Taking one tile from each half of the workgroup's rows gives every
@@ -86,10 +89,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const bool ok = myq[t] < nb;
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc)
-            qreg[t][kc] = ok ? gload8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : vec8<T>{};
+            qreg[t][kc] = (ok && 16 * kc + 8 * g < dg)
+                              ? gload8(qh + (long)myq[t] * dg + 16 * kc + 8 * g) : vec8<T>{};
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
-            oreg[t][kc] = ok ? gload8(oh + (long)myq[t] * DV + 16 * kc + 8 * g) : vec8<T>{};
+            oreg[t][kc] = (ok && 16 * kc + 8 * g < dvg)
+                              ? gload8(oh + (long)myq[t] * dvg + 16 * kc + 8 * g) : vec8<T>{};
         // Q and dO rows are only MFMA inputs: keep them in AGPRs, leaving
         // the VGPRs to the S, dP and dS tiles of a 64-key step
 #pragma unroll
@@ -116,12 +121,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead.
     // Rows past mb (last tile only) come back as zeros; masked steps zero
     // their P.
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * D * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * DV * 2);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * dg * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * dvg * 2);
     TileLoader<D, BN, NW> ldK;
-    ldK.init(wave, lane);
+    ldK.init(wave, lane, dg);
     TileLoader<DV, BN, NW> ldV;
-    ldV.init(wave, lane);
+    ldV.init(wave, lane, dvg);
     auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
         tile_fill<D, BN, NW>(ldK, Kbuf(buf_), rK, k0, wave);
         tile_fill<DV, BN, NW>(ldV, Vbuf(buf_), rV, k0, wave);
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (myq[t] < n) {
-            T* qrow = dq + (bh * (long)n + myq[t]) * D;
+            T* qrow = dq + (bh * (long)n + myq[t]) * dg;
 #pragma unroll
             for (int x = 0; x < D / 32; ++x) {
 #pragma unroll
@@ -288,7 +293,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     vec4<T> w;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) w[r] = (T)(acc[x][t][4 * vq + r] * scale);
-                    *reinterpret_cast<vec4<T>*>(qrow + 32 * x + 8 * vq + 4 * g) = w;
+                    const int col = 32 * x + 8 * vq + 4 * g;
+                    if (col < dg) *reinterpret_cast<vec4<T>*>(qrow + col) = w;
                 }
             }
         }
@@ -305,11 +311,11 @@ void launch_dq(const Problem& p, const void* q, const void* k, const void* v, co
     if (p.causal)
         bwd_dq_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2, si);
+            (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
     else
         bwd_dq_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dq, p.n, p.m, w.n_pad, p.scale, c2, si);
+            (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
 }
 
 }  // namespace
@@ -317,10 +323,13 @@ void launch_dq(const Problem& p, const void* q, const void* k, const void* v, co
 template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const Workspace& w, void* dq, hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch_dq<T, 64, 64>(p, q, k, v, dout, w, dq, s);
-    else if (p.d == 128 && p.dv == 128) launch_dq<T, 128, 128>(p, q, k, v, dout, w, dq, s);
-    else if (p.d == 128 && p.dv == 64) launch_dq<T, 128, 64>(p, q, k, v, dout, w, dq, s);
-    else return false;
+    switch (mfma_widths(p)) {
+    case 0x4040: launch_dq<T, 64, 64>(p, q, k, v, dout, w, dq, s); break;
+    case 0x4080: launch_dq<T, 64, 128>(p, q, k, v, dout, w, dq, s); break;
+    case 0x8040: launch_dq<T, 128, 64>(p, q, k, v, dout, w, dq, s); break;
+    case 0x8080: launch_dq<T, 128, 128>(p, q, k, v, dout, w, dq, s); break;
+    default: return false;
+    }
     return true;
 }
 

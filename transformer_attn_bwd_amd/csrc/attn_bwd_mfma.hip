@@ -28,8 +28,8 @@ namespace {
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ lse2, float* __restrict__ Dw, int n, int n_pad, long total_rows,
-    SeqInfo si) {
+    float* __restrict__ lse2, float* __restrict__ Dw, int n, int dvg, int n_pad,
+    long total_rows, SeqInfo si) {
     constexpr int LPR = DV / 8;        // lanes per row, 8 elements (16 bytes) each
     constexpr int RPB = 256 / LPR;     // rows per block
     const int tid = threadIdx.x;
@@ -40,8 +40,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     const int i = valid_row ? (int)(row % n_pad) : 0;
     const int nb = seq_lens(si, bh, n, 1).n;
     float acc = 0.f;
-    if (valid_row && i < nb) {
-        const long off = (bh * (long)n + i) * DV + 8 * part;
+    // rows hold dvg <= DV elements; lanes past them add nothing
+    if (valid_row && i < nb && 8 * part < dvg) {
+        const long off = (bh * (long)n + i) * dvg + 8 * part;
         vec8<T> a = gload8(o + off);
         vec8<T> b = gload8(dout + off);
 #pragma unroll
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ Dw, T* __restrict__ dk, T* __restrict__ dvo, int n, int m,
-    int n_pad, float scale, float c2, SeqInfo si) {
+    int dg, int dvg, int n_pad, float scale, float c2, SeqInfo si) {
     using C = DkdvCfg<D, DV>;
     using SC = DkdvSched<D, DV>;
     constexpr int BM = C::BM, NW = C::NW, LA = C::LA;
@@ -158,10 +159,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const SeqLens len = seq_lens(si, bh, n, m);
     const int nb = len.n, mb = len.m, off = len.off;
 
-    const T* qh = q + bh * (long)n * D;
-    const T* kh = k + bh * (long)m * D;
-    const T* vh = v + bh * (long)m * DV;
-    const T* oh = dout + bh * (long)n * DV;
+    // Rows of Q and K hold dg <= D elements, rows of V and dO dvg <= DV (each
+    // a multiple of 8); the columns past them are zeros in registers and
+    // LDS, so they add nothing to any product.
+    const T* qh = q + bh * (long)n * dg;
+    const T* kh = k + bh * (long)m * dg;
+    const T* vh = v + bh * (long)m * dvg;
+    const T* oh = dout + bh * (long)n * dvg;
     const float* lh = lse2 + bh * (long)n_pad;
     const float* dh = Dw + bh * (long)n_pad;
 
@@ -169,8 +173,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // P only reach dK and dV rows that are written as zeros).
     {
         TileLoader<D, C::BN, NW> ldK;
-        ldK.init(wave, lane);
-        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)mb * D * 2), j0, wave);
+        ldK.init(wave, lane, dg);
+        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)mb * dg * 2), j0, wave);
     }
     // This lane's V row for key tile kt (key kw0 + 32 kt + li): B operand of
     // dP = dO V^T.
@@ -180,7 +184,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int key = kw0 + 32 * kt + li;
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
-            vreg[kt][kc] = key < mb ? gload8(vh + (long)key * DV + 16 * kc + 8 * g) : vec8<T>{};
+            vreg[kt][kc] = (key < mb && 16 * kc + 8 * g < dvg)
+                               ? gload8(vh + (long)key * dvg + 16 * kc + 8 * g) : vec8<T>{};
     }
 
     TileOffsets<D> toQ;
@@ -206,14 +211,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Query tile i0 into a buffer: Q and dO rows (rows past nb come back as
     // zeros; their LSE2 is +inf, so P = 0 and they contribute nothing), and
     // the per-row LSE2 and D.
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)nb * D * 2);
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)nb * DV * 2);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)nb * dg * 2);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)nb * dvg * 2);
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(lh, (uint32_t)n_pad * 4);
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(dh, (uint32_t)n_pad * 4);
     TileLoader<D, BM, NW> ldQ;
-    ldQ.init(wave, lane);
+    ldQ.init(wave, lane, dg);
     TileLoader<DV, BM, NW> ldO;
-    ldO.init(wave, lane);
+    ldO.init(wave, lane, dvg);
     auto stage = [&](auto buf_, int i0) __attribute__((always_inline)) {
         tile_fill<D, BM, NW>(ldQ, pick(buf_, sQ0, sQ1), rQ, i0, wave);
         tile_fill<DV, BM, NW>(ldO, pick(buf_, sO0, sO1), rO, i0, wave);
@@ -386,8 +391,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Accumulator slot vv of tile (kt, x) holds key kw0 + 32kt + 8(vv>>2) +
     // 4g + (vv&3), column 32x + li.  Keys past mb are padding: zeros.
-    T* dkh = dk + bh * (long)m * D;
-    T* dvh = dvo + bh * (long)m * DV;
+    T* dkh = dk + bh * (long)m * dg;
+    T* dvh = dvo + bh * (long)m * dvg;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -400,10 +405,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 const bool real = key < mb;
 #pragma unroll
                 for (int x = 0; x < D / 32; ++x)
-                    dkh[(long)key * D + 32 * x + li] = real ? (T)(accK[kt][x][vv] * scale) : (T)0.f;
+                    if (32 * x + li < dg)
+                        dkh[(long)key * dg + 32 * x + li] =
+                            real ? (T)(accK[kt][x][vv] * scale) : (T)0.f;
 #pragma unroll
                 for (int x = 0; x < DV / 32; ++x)
-                    dvh[(long)key * DV + 32 * x + li] = real ? (T)accV[kt][x][vv] : (T)0.f;
+                    if (32 * x + li < dvg)
+                        dvh[(long)key * dvg + 32 * x + li] = real ? (T)accV[kt][x][vv] : (T)0.f;
             }
         }
     }
@@ -416,7 +424,7 @@ void launch_pre(const Problem& p, const void* o, const void* dout, const float* 
     const long total = p.heads() * (long)w.n_pad;
     const unsigned blocks = (unsigned)((total + RPB - 1) / RPB);
     bwd_preprocess_kernel<T, DV><<<blocks, 256, 0, s>>>((const T*)o, (const T*)dout, lse,
-                                                        w.lse2, w.D, p.n, w.n_pad, total,
+                                                        w.lse2, w.D, p.n, p.dv, w.n_pad, total,
                                                         seq_info(p));
 }
 
@@ -430,11 +438,11 @@ void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
     if (p.causal)
         bwd_dkdv_kernel<T, D, DV, true><<<grid, 256, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2, si);
+            (T*)dk, (T*)dv, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
     else
         bwd_dkdv_kernel<T, D, DV, false><<<grid, 256, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dk, (T*)dv, p.n, p.m, w.n_pad, p.scale, c2, si);
+            (T*)dk, (T*)dv, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
 }
 
 }  // namespace
@@ -442,9 +450,11 @@ void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
 template <typename T>
 bool launch_bwd_preprocess_mfma(const Problem& p, const void* o, const void* dout,
                                 const float* lse, const Workspace& w, hipStream_t s) {
-    if (p.dv == 64) launch_pre<T, 64>(p, o, dout, lse, w, s);
-    else if (p.dv == 128) launch_pre<T, 128>(p, o, dout, lse, w, s);
-    else return false;
+    switch (mfma_widths(p) & 0xff) {
+    case 0x40: launch_pre<T, 64>(p, o, dout, lse, w, s); break;
+    case 0x80: launch_pre<T, 128>(p, o, dout, lse, w, s); break;
+    default: return false;
+    }
     return true;
 }
 
@@ -452,10 +462,13 @@ template <typename T>
 bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
                           const void* dout, const Workspace& w, void* dk, void* dv,
                           hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch_dkdv<T, 64, 64>(p, q, k, v, dout, w, dk, dv, s);
-    else if (p.d == 128 && p.dv == 128) launch_dkdv<T, 128, 128>(p, q, k, v, dout, w, dk, dv, s);
-    else if (p.d == 128 && p.dv == 64) launch_dkdv<T, 128, 64>(p, q, k, v, dout, w, dk, dv, s);
-    else return false;
+    switch (mfma_widths(p)) {
+    case 0x4040: launch_dkdv<T, 64, 64>(p, q, k, v, dout, w, dk, dv, s); break;
+    case 0x4080: launch_dkdv<T, 64, 128>(p, q, k, v, dout, w, dk, dv, s); break;
+    case 0x8040: launch_dkdv<T, 128, 64>(p, q, k, v, dout, w, dk, dv, s); break;
+    case 0x8080: launch_dkdv<T, 128, 128>(p, q, k, v, dout, w, dk, dv, s); break;
+    default: return false;
+    }
     return true;
 }
 

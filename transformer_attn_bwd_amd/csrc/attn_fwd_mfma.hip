@@ -38,7 +38,8 @@ constexpr float kRescaleThreshold = 8.f;     // log2 of the largest P allowed
 template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    T* __restrict__ o, float* __restrict__ lse, int n, int m, float c2, SeqInfo si) {
+    T* __restrict__ o, float* __restrict__ lse, int n, int m, int dg, int dvg, float c2,
+    SeqInfo si) {
     using C = FwdCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     constexpr int KA = D / 16, NXV = DV / 32;
@@ -63,9 +64,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const SeqLens len = seq_lens(si, bh, n, m);
     const int nb = len.n, mb = len.m, off = len.off;
 
-    const T* qh = q + bh * (long)n * D;
-    const T* kh = k + bh * (long)m * D;
-    const T* vh = v + bh * (long)m * DV;
+    // Rows of Q and K hold dg <= D elements, rows of V and O dvg <= DV (each
+    // a multiple of 8); the columns past them are zeros in registers and
+    // LDS, so they add nothing to any product.
+    const T* qh = q + bh * (long)n * dg;
+    const T* kh = k + bh * (long)m * dg;
+    const T* vh = v + bh * (long)m * dvg;
 
     // A negative scale is handled by negating Q, so that the row max of
     // S * c2 is c2 times the row max of the computed S.
@@ -82,7 +86,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const bool ok = myq[t] < nb;
 #pragma unroll
         for (int kc = 0; kc < KA; ++kc) {
-            vec8<T> x = ok ? gload8(qh + (long)myq[t] * D + 16 * kc + 8 * g) : vec8<T>{};
+            const bool in = ok && 16 * kc + 8 * g < dg;
+            vec8<T> x = in ? gload8(qh + (long)myq[t] * dg + 16 * kc + 8 * g) : vec8<T>{};
             if (neg) x = __builtin_bit_cast(vec8<T>, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
             qreg[t][kc] = x;
             // keep the Q operands in AGPRs (MFMAs read them from there), so
@@ -106,12 +111,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead;
     // rows past mb come back as zeros and are masked.
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * D * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * DV * 2);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * dg * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * dvg * 2);
     TileLoader<D, BN, NW> ldK;
-    ldK.init(wave, lane);
+    ldK.init(wave, lane, dg);
     TileLoader<DV, BN, NW> ldV;
-    ldV.init(wave, lane);
+    ldV.init(wave, lane, dvg);
     auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
         tile_fill<D, BN, NW>(ldK, pick(buf_, sK0, sK1), rK, k0, wave);
         tile_fill<DV, BN, NW>(ldV, pick(buf_, sV0, sV1), rV, k0, wave);
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const bool seen = myq[t] < nb && l_tot > 0.f;
         const float inv = seen ? 1.f / l_tot : 0.f;
         if (myq[t] < n) {
-            T* orow = o + (bh * (long)n + myq[t]) * DV;
+            T* orow = o + (bh * (long)n + myq[t]) * dvg;
 #pragma unroll
             for (int x = 0; x < NXV; ++x) {
 #pragma unroll
@@ -300,7 +305,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     vec4<T> w;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) w[r] = (T)(acc[x][t][4 * vq + r] * inv);
-                    *reinterpret_cast<vec4<T>*>(orow + 32 * x + 8 * vq + 4 * g) = w;
+                    const int col = 32 * x + 8 * vq + 4 * g;
+                    if (col < dvg) *reinterpret_cast<vec4<T>*>(orow + col) = w;
                 }
             }
             if (g == 0)
@@ -318,10 +324,10 @@ void launch(const Problem& p, const void* q, const void* k, const void* v, void*
     const SeqInfo si = seq_info(p);
     if (p.causal)
         fwd_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
-            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2, si);
+            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, p.d, p.dv, c2, si);
     else
         fwd_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
-            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, c2, si);
+            (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, p.n, p.m, p.d, p.dv, c2, si);
 }
 
 }  // namespace
@@ -329,10 +335,13 @@ void launch(const Problem& p, const void* q, const void* k, const void* v, void*
 template <typename T>
 bool launch_fwd_mfma(const Problem& p, const void* q, const void* k, const void* v, void* o,
                      float* lse, hipStream_t s) {
-    if (p.d == 64 && p.dv == 64) launch<T, 64, 64>(p, q, k, v, o, lse, s);
-    else if (p.d == 128 && p.dv == 128) launch<T, 128, 128>(p, q, k, v, o, lse, s);
-    else if (p.d == 128 && p.dv == 64) launch<T, 128, 64>(p, q, k, v, o, lse, s);
-    else return false;
+    switch (mfma_widths(p)) {
+    case 0x4040: launch<T, 64, 64>(p, q, k, v, o, lse, s); break;
+    case 0x4080: launch<T, 64, 128>(p, q, k, v, o, lse, s); break;
+    case 0x8040: launch<T, 128, 64>(p, q, k, v, o, lse, s); break;
+    case 0x8080: launch<T, 128, 128>(p, q, k, v, o, lse, s); break;
+    default: return false;
+    }
     return true;
 }
 

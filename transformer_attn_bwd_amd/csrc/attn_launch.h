@@ -28,6 +28,15 @@ struct Problem {
     long heads() const { return B * H; }
 };
 
+// Tile widths the 16-bit kernels use for head widths d and dv: 64 or 128
+// each (the head padded with zero columns), as 0xDDVV; 0 if d or dv is not
+// a multiple of 8 in 8..128.
+inline int mfma_widths(const Problem& p) {
+    auto tile = [](int x) { return (x < 8 || x > 128 || x % 8) ? 0 : (x <= 64 ? 64 : 128); };
+    const int td = tile(p.d), tv = tile(p.dv);
+    return (td && tv) ? (td << 8) | tv : 0;
+}
+
 // What the kernels need to find a head's lengths and causal offset.
 struct SeqInfo {
     const int* sq;     // per-batch query lengths or null
