@@ -68,6 +68,17 @@ enum attn_mask {
                                           sees the last key */
 };
 
+/*
+ * Tensor layouts of attn_fwd_ex / attn_bwd_ex (all of q, k, v, o, dout, dq,
+ * dk, dv_out; lse is always [B, H, n]).  ATTN_LAYOUT_BSHD is what a
+ * projection X W produces for all heads at once, so no transpose is needed
+ * between the projections and attention.
+ */
+enum attn_layout {
+    ATTN_LAYOUT_BHSD = 0,              /* [B, H, seq, dim], each head contiguous */
+    ATTN_LAYOUT_BSHD = 1               /* [B, seq, H, dim], the heads of a row adjacent */
+};
+
 /* Return codes. */
 enum attn_status {
     ATTN_OK = 0,
@@ -110,14 +121,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * [0, m] are clamped into them (the library cannot check device values
  * without synchronising).  Padded query rows, and rows that see no key
  * (m_b == 0, or i < n_b - m_b under ATTN_MASK_CAUSAL_BOTTOM_RIGHT), are
- * written as o = 0 and lse = -inf.  No n == m requirement.  Otherwise as
- * attn_fwd, which is attn_fwd_ex with NULL lengths and mask
- * ATTN_MASK_CAUSAL or ATTN_MASK_NONE.
+ * written as o = 0 and lse = -inf.  No n == m requirement.  layout is an
+ * enum attn_layout; with ATTN_LAYOUT_BSHD and a 16-bit dtype,
+ * max(n, m) * H * max(d, dv) * 2 must not exceed 2^30 (ATTN_EUNSUPPORTED).
+ * Otherwise as attn_fwd, which is attn_fwd_ex with NULL lengths, mask
+ * ATTN_MASK_CAUSAL or ATTN_MASK_NONE and ATTN_LAYOUT_BHSD.
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 const int* seqlens_q, const int* seqlens_k,
                 int B, int H, int n, int m, int d, int dv, float scale, int mask,
-                int dtype, void* stream);
+                int layout, int dtype, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd needs for these sizes (a multiple of
@@ -149,7 +162,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 const float* lse, void* dq, void* dk, void* dv_out,
                 const int* seqlens_q, const int* seqlens_k,
                 int B, int H, int n, int m, int d, int dv, float scale, int mask,
-                int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream);
+                int layout, int dtype, int flags, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /* Static string naming a status code. */
 const char* attn_status_str(int status);

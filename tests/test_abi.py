@@ -150,17 +150,17 @@ def test_binding_constants_match_header():
     assert vals == {"ATTN_F32": B.ATTN_F32, "ATTN_BF16": B.ATTN_BF16, "ATTN_F16": B.ATTN_F16}
 
 
-def _fwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, dtype=B.ATTN_BF16,
-            sq=None, sk=None, ptrs=None):
+def _fwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, layout=0,
+            dtype=B.ATTN_BF16, sq=None, sk=None, ptrs=None):
     p = ptrs if ptrs is not None else [FAKE] * 5
-    return lib.attn_fwd_ex(*p, sq, sk, B_, H, n, m, d, dv, scale, mask, dtype, NULL)
+    return lib.attn_fwd_ex(*p, sq, sk, B_, H, n, m, d, dv, scale, mask, layout, dtype, NULL)
 
 
-def _bwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, dtype=B.ATTN_BF16,
-            flags=0, sq=None, sk=None, ws=FAKE, ws_bytes=1 << 30, ptrs=None):
+def _bwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, layout=0,
+            dtype=B.ATTN_BF16, flags=0, sq=None, sk=None, ws=FAKE, ws_bytes=1 << 30, ptrs=None):
     p = ptrs if ptrs is not None else [FAKE] * 9
-    return lib.attn_bwd_ex(*p, sq, sk, B_, H, n, m, d, dv, scale, mask, dtype, flags, ws,
-                           ws_bytes, NULL)
+    return lib.attn_bwd_ex(*p, sq, sk, B_, H, n, m, d, dv, scale, mask, layout, dtype, flags,
+                           ws, ws_bytes, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -170,6 +170,9 @@ def _bwd_ex(lib, B_=1, H=1, n=64, m=64, d=64, dv=64, scale=0.125, mask=0, dtype=
     (dict(m=0), B.ATTN_EINVAL),
     (dict(scale=float("nan")), B.ATTN_EINVAL),
     (dict(d=100, dv=96), B.ATTN_EUNSUPPORTED),
+    (dict(layout=2), B.ATTN_EUNSUPPORTED),
+    (dict(layout=B.ATTN_LAYOUT_BSHD, H=4096, n=1 << 20, m=1 << 20, d=128, dv=128),
+     B.ATTN_EUNSUPPORTED),   # a head's rows would span more than 2^30 bytes
     (dict(sq=ctypes.c_void_p((1 << 20) + 2)), B.ATTN_EINVAL),
     (dict(sk=ctypes.c_void_p((1 << 20) + 1)), B.ATTN_EINVAL),
 ])
@@ -205,3 +208,11 @@ def test_mask_constants_match_header():
     vals = dict((k.strip(), int(v)) for k, v in (e.split("=") for e in body.split(",") if "=" in e))
     assert vals == {"ATTN_MASK_NONE": B.ATTN_MASK_NONE, "ATTN_MASK_CAUSAL": B.ATTN_MASK_CAUSAL,
                     "ATTN_MASK_CAUSAL_BOTTOM_RIGHT": B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT}
+
+
+def test_layout_constants_match_header():
+    text = open(HEADER).read()
+    body = re.search(r"enum attn_layout \{(.*?)\};", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    vals = dict((k.strip(), int(v)) for k, v in (e.split("=") for e in body.split(",") if "=" in e))
+    assert vals == {"ATTN_LAYOUT_BHSD": B.ATTN_LAYOUT_BHSD, "ATTN_LAYOUT_BSHD": B.ATTN_LAYOUT_BSHD}

@@ -37,19 +37,27 @@ def _inputs(B, H, n, m, d, dv, dtype, seed, lq, lk, mult=1.0):
     return q, k, v, do
 
 
-def _run(case):
+def _run(case, layout="bhsd"):
     (name, B, H, n, m, d, dv, dtype, mask, lq, lk, seed) = case
-    say(f"case {name}: B={B} H={H} n={n} m={m} d={d} dv={dv} {dtype} mask={mask} lq={lq} lk={lk}")
+    say(f"case {name}: B={B} H={H} n={n} m={m} d={d} dv={dv} {dtype} mask={mask} lq={lq} "
+        f"lk={lk} layout={layout}")
     q, k, v, do = _inputs(B, H, n, m, d, dv, dtype, seed, lq, lk)
     dev = "cuda:0"
-    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    # [B, seq, H, dim] copies for the bshd layout; results are viewed back
+    # as [B, H, seq, dim] for the comparison
+    to_dev = (lambda t: t.transpose(1, 2).contiguous().to(dev)) if layout == "bshd" else \
+        (lambda t: t.to(dev))
+    back = (lambda t: t.transpose(1, 2)) if layout == "bshd" else (lambda t: t)
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
     sq = torch.tensor(lq, dtype=torch.int32, device=dev) if lq is not None else None
     sk = torch.tensor(lk, dtype=torch.int32, device=dev) if lk is not None else None
     scale = 1.0 / np.sqrt(d)
-    o, lse = attn.fwd(qd, kd, vd, scale=scale, mask=mask, seqlens_q=sq, seqlens_k=sk)
+    o, lse = attn.fwd(qd, kd, vd, scale=scale, mask=mask, seqlens_q=sq, seqlens_k=sk,
+                      layout=layout)
     dq, dk, dvv = attn.bwd(qd, kd, vd, o, dod, lse, scale=scale, mask=mask, seqlens_q=sq,
-                           seqlens_k=sk)
+                           seqlens_k=sk, layout=layout)
     torch.cuda.synchronize()
+    o, dq, dk, dvv = back(o), back(dq), back(dk), back(dvv)
     ref = oracle.attn_bwd_masked(torch.nan_to_num(q), torch.nan_to_num(k), torch.nan_to_num(v),
                                  torch.nan_to_num(do), scale=scale, mask=mask,
                                  seqlens_q=lq, seqlens_k=lk)
@@ -105,6 +113,24 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_masked_parity(case):
     _run(case)
+
+
+BSHD_CASES = [
+    ("bshd_causal_d128", 2, 3, 300, 300, 128, 128, "bf16", "causal", None, None, 140),
+    ("bshd_none_d64_dv128", 1, 4, 130, 333, 64, 128, "bf16", "none", None, None, 141),
+    ("bshd_varlen_br_d96", 3, 2, 400, 500, 96, 96, "bf16", "causal_bottom_right",
+     [400, 33, 250], [500, 90, 250], 142),
+    ("bshd_fp16_d128_dv64", 2, 2, 257, 257, 128, 64, "fp16", "causal", [257, 200], [257, 200],
+     143),
+    ("bshd_fp32", 2, 3, 50, 70, 40, 24, "fp32", "causal_bottom_right", [50, 20], [70, 31], 144),
+]
+
+
+@pytest.mark.parametrize("case", BSHD_CASES, ids=lambda c: c[0])
+def test_bshd_layout_parity(case):
+    """[B, seq, H, dim] tensors (what a fused projection produces): same
+    results as the oracle on the [B, H, seq, dim] view."""
+    _run(case, layout="bshd")
 
 
 def test_full_lengths_match_plain_entry_points():

@@ -24,6 +24,8 @@ ATTN_DQ_AUTO, ATTN_DQ_SEPARATE = 0, 1
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
          "causal_bottom_right": ATTN_MASK_CAUSAL_BOTTOM_RIGHT}
+ATTN_LAYOUT_BHSD, ATTN_LAYOUT_BSHD = 0, 1
+LAYOUTS = {"bhsd": ATTN_LAYOUT_BHSD, "bshd": ATTN_LAYOUT_BSHD}
 ATTN_STAGE_PREPROCESS, ATTN_STAGE_DKDV, ATTN_STAGE_DQ = 1 << 8, 1 << 9, 1 << 10
 DQ_MODES = {"auto": ATTN_DQ_AUTO, "separate": ATTN_DQ_SEPARATE}
 STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
@@ -56,9 +58,9 @@ def load():
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_bwd.argtypes = [vp] * 9 + [I] * 6 + [F, I, I, I, vp, Z, vp]
     lib.attn_bwd.restype = I
-    lib.attn_fwd_ex.argtypes = [vp] * 7 + [I] * 6 + [F, I, I, vp]
+    lib.attn_fwd_ex.argtypes = [vp] * 7 + [I] * 6 + [F, I, I, I, vp]
     lib.attn_fwd_ex.restype = I
-    lib.attn_bwd_ex.argtypes = [vp] * 11 + [I] * 6 + [F, I, I, I, vp, Z, vp]
+    lib.attn_bwd_ex.argtypes = [vp] * 11 + [I] * 6 + [F, I, I, I, I, vp, Z, vp]
     lib.attn_bwd_ex.restype = I
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -95,9 +97,13 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _shape(q, k, v):
+def _shape(q, k, v, layout="bhsd"):
+    """(B, H, n, m, d, dv) of [B, H, seq, dim] ("bhsd") or [B, seq, H, dim]
+    ("bshd") tensors."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-d [B, H, seq, dim]")
+        raise ValueError("q, k, v must be 4-d")
+    if layout == "bshd":
+        q, k, v = (t.transpose(1, 2) for t in (q, k, v))   # shape arithmetic only
     B, H, n, d = q.shape
     m, dv = v.shape[2], v.shape[3]
     if tuple(k.shape) != (B, H, m, d) or tuple(v.shape[:2]) != (B, H):
@@ -124,25 +130,27 @@ def _mask_code(causal, mask):
 
 
 def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, mask=None, seqlens_q=None,
-        seqlens_k=None):
+        seqlens_k=None, layout="bhsd"):
     """O [B,H,n,dv] (q's dtype) and LSE [B,H,n] (float32, natural log).
 
     ``causal=True`` is the causal mask with n == m.  ``mask`` ("none",
     "causal" or "causal_bottom_right") and the per-batch lengths
     ``seqlens_q`` / ``seqlens_k`` (int32 [B] on the GPU) select the general
-    entry point, attn_fwd_ex.
+    entry point, attn_fwd_ex, and so does ``layout="bshd"`` ([B, seq, H, dim]
+    tensors; LSE stays [B, H, n]).
     """
     lib = load()
     _check_dev(q, k, v)
-    B, H, n, m, d, dv = _shape(q, k, v)
+    B, H, n, m, d, dv = _shape(q, k, v, layout)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=q.device)
+        oshape = (B, n, H, dv) if layout == "bshd" else (B, H, n, dv)
+        out = torch.empty(oshape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
     _check_dev(out, lse)
-    if mask is None and seqlens_q is None and seqlens_k is None:
+    if mask is None and seqlens_q is None and seqlens_k is None and layout == "bhsd":
         st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n, m, d, dv,
                           float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
         where = "attn_fwd"
@@ -150,7 +158,8 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, mask=None, seqlen
         code = _mask_code(causal, mask)
         sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
         st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sq), _ptr(sk),
-                             B, H, n, m, d, dv, float(scale), code, _dtype_code(q), _stream(q))
+                             B, H, n, m, d, dv, float(scale), code, LAYOUTS[layout],
+                             _dtype_code(q), _stream(q))
         where = "attn_fwd_ex"
     if st != ATTN_OK:
         raise AttnError(st, where)
@@ -165,16 +174,17 @@ def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto")
 
 
 def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace=None,
-        dq=None, dk=None, dv=None, stages=None, mask=None, seqlens_q=None, seqlens_k=None):
+        dq=None, dk=None, dv=None, stages=None, mask=None, seqlens_q=None, seqlens_k=None,
+        layout="bhsd"):
     """(dq, dk, dv) with the shapes and dtype of (q, k, v).
 
     ``stages`` (a subset of {"preprocess", "dkdv", "dq"}) restricts which
     kernels run; it exists for timing single kernels.  ``mask`` and the
-    per-batch lengths select attn_bwd_ex, as in fwd().
+    per-batch lengths and ``layout`` select attn_bwd_ex, as in fwd().
     """
     lib = load()
     _check_dev(q, k, v, o, do, lse)
-    B, H, n, m, d, dvw = _shape(q, k, v)
+    B, H, n, m, d, dvw = _shape(q, k, v, layout)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     flags = DQ_MODES[dq_mode]
@@ -190,7 +200,7 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     dv = torch.empty_like(v) if dv is None else dv
     _check_dev(dq, dk, dv, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if mask is None and seqlens_q is None and seqlens_k is None:
+    if mask is None and seqlens_q is None and seqlens_k is None and layout == "bhsd":
         st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                           _ptr(dk), _ptr(dv), B, H, n, m, d, dvw, float(scale),
                           int(bool(causal)), code, flags, _ptr(workspace), ws_bytes, _stream(q))
@@ -200,8 +210,8 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
         sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
         st = lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(sq), _ptr(sk), B, H, n, m, d, dvw,
-                             float(scale), mcode, code, flags, _ptr(workspace), ws_bytes,
-                             _stream(q))
+                             float(scale), mcode, LAYOUTS[layout], code, flags, _ptr(workspace),
+                             ws_bytes, _stream(q))
         where = "attn_bwd_ex"
     if st != ATTN_OK:
         raise AttnError(st, where)

@@ -62,6 +62,19 @@ int check_problem(int B, int H, int n, int m, int d, int dv, float scale, int ma
 // Per-batch length arrays: NULL, or 4-byte aligned device memory.
 bool lens_ok(const int* p) { return p == nullptr || aligned(p, 4); }
 
+// Memory layout of the tensors; the 16-bit kernels address one head's rows
+// through 32-bit buffer offsets, so a head's byte range must stay within
+// 2^30 (always true for [B, H, seq, dim]).
+int set_layout(Problem* p, int layout) {
+    if (layout != ATTN_LAYOUT_BHSD && layout != ATTN_LAYOUT_BSHD) return ATTN_EUNSUPPORTED;
+    p->bshd = layout == ATTN_LAYOUT_BSHD;
+    if (p->bshd && p->dtype != ATTN_F32) {
+        const long rows = p->n > p->m ? p->n : p->m, w = p->d > p->dv ? p->d : p->dv;
+        if (rows * p->H * w * 2 > (1L << 30)) return ATTN_EUNSUPPORTED;
+    }
+    return ATTN_OK;
+}
+
 // A tensor with elements needs a non-null pointer aligned for the kernels'
 // vector accesses (16 bytes for 16-bit rows, 4 bytes for float32).
 bool tensor_ok(const void* p, long elems, int dtype) {
@@ -101,10 +114,11 @@ const char* attn_status_str(int status) {
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 const int* seqlens_q, const int* seqlens_k, int B, int H, int n, int m, int d,
-                int dv, float scale, int mask, int dtype, void* stream) {
+                int dv, float scale, int mask, int layout, int dtype, void* stream) {
     Problem p;
     int st = check_problem(B, H, n, m, d, dv, scale, mask, dtype, &p);
     if (st != ATTN_OK) return st;
+    if ((st = set_layout(&p, layout)) != ATTN_OK) return st;
     if (!lens_ok(seqlens_q) || !lens_ok(seqlens_k)) return ATTN_EINVAL;
     p.seqlens_q = seqlens_q;
     p.seqlens_k = seqlens_k;
@@ -133,7 +147,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (st != ATTN_OK) return st;
     if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
     return attn_fwd_ex(q, k, v, o, lse, nullptr, nullptr, B, H, n, m, d, dv, scale,
-                       causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE, dtype, stream);
+                       causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE, ATTN_LAYOUT_BHSD, dtype,
+                       stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
@@ -147,11 +162,12 @@ size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int d
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
                 const float* lse, void* dq, void* dk, void* dv_out, const int* seqlens_q,
                 const int* seqlens_k, int B, int H, int n, int m, int d, int dv, float scale,
-                int mask, int dtype, int flags, void* workspace, size_t workspace_bytes_given,
-                void* stream) {
+                int mask, int layout, int dtype, int flags, void* workspace,
+                size_t workspace_bytes_given, void* stream) {
     Problem p;
     int st = check_problem(B, H, n, m, d, dv, scale, mask, dtype, &p);
     if (st != ATTN_OK) return st;
+    if ((st = set_layout(&p, layout)) != ATTN_OK) return st;
     if (!lens_ok(seqlens_q) || !lens_ok(seqlens_k)) return ATTN_EINVAL;
     p.seqlens_q = seqlens_q;
     p.seqlens_k = seqlens_k;
@@ -223,8 +239,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (st != ATTN_OK) return st;
     if (causal && n != m) return ATTN_ECAUSAL_SHAPE;
     return attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv_out, nullptr, nullptr, B, H, n, m, d,
-                       dv, scale, causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE, dtype, flags,
-                       workspace, workspace_bytes_given, stream);
+                       dv, scale, causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE, ATTN_LAYOUT_BHSD,
+                       dtype, flags, workspace, workspace_bytes_given, stream);
 }
 
 }  // extern "C"

@@ -71,10 +71,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Rows of Q and K hold dg <= D elements, rows of V and dO dvg <= DV (each
     // a multiple of 8); the columns past them are zeros in registers and
     // LDS, so they add nothing to any product.
-    const T* qh = q + bh * (long)n * dg;
-    const T* kh = k + bh * (long)m * dg;
-    const T* vh = v + bh * (long)m * dvg;
-    const T* oh = dout + bh * (long)n * dvg;
+    const HeadView hq = head_view(si, bh, n, dg), hk = head_view(si, bh, m, dg);
+    const HeadView hv = head_view(si, bh, m, dvg), ho = head_view(si, bh, n, dvg);
+    const T* qh = q + hq.base;
+    const T* kh = k + hk.base;
+    const T* vh = v + hv.base;
+    const T* oh = dout + ho.base;
 
     // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31).
     // Taking one tile from each half of the workgroup's rows gives every
@@ -90,11 +92,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc)
             qreg[t][kc] = (ok && 16 * kc + 8 * g < dg)
-                              ? gload8(qh + (long)myq[t] * dg + 16 * kc + 8 * g) : vec8<T>{};
+                              ? gload8(qh + (long)myq[t] * hq.stride + 16 * kc + 8 * g)
+                              : vec8<T>{};
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
             oreg[t][kc] = (ok && 16 * kc + 8 * g < dvg)
-                              ? gload8(oh + (long)myq[t] * dvg + 16 * kc + 8 * g) : vec8<T>{};
+                              ? gload8(oh + (long)myq[t] * ho.stride + 16 * kc + 8 * g)
+                              : vec8<T>{};
         // Q and dO rows are only MFMA inputs: keep them in AGPRs, leaving
         // the VGPRs to the S, dP and dS tiles of a 64-key step
 #pragma unroll
@@ -121,12 +125,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead.
     // Rows past mb (last tile only) come back as zeros; masked steps zero
     // their P.
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * dg * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * dvg * 2);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * hk.stride * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * hv.stride * 2);
     TileLoader<D, BN, NW> ldK;
-    ldK.init(wave, lane, dg);
+    ldK.init(wave, lane, dg, hk.stride);
     TileLoader<DV, BN, NW> ldV;
-    ldV.init(wave, lane, dvg);
+    ldV.init(wave, lane, dvg, hv.stride);
     auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
         tile_fill<D, BN, NW>(ldK, Kbuf(buf_), rK, k0, wave);
         tile_fill<DV, BN, NW>(ldV, Vbuf(buf_), rV, k0, wave);
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (myq[t] < n) {
-            T* qrow = dq + (bh * (long)n + myq[t]) * dg;
+            T* qrow = dq + hq.base + (long)myq[t] * hq.stride;
 #pragma unroll
             for (int x = 0; x < D / 32; ++x) {
 #pragma unroll

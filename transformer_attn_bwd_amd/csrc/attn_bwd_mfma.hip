@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     float acc = 0.f;
     // rows hold dvg <= DV elements; lanes past them add nothing
     if (valid_row && i < nb && 8 * part < dvg) {
-        const long off = (bh * (long)n + i) * dvg + 8 * part;
+        const HeadView hv = head_view(si, bh, n, dvg);
+        const long off = hv.base + (long)i * hv.stride + 8 * part;
         vec8<T> a = gload8(o + off);
         vec8<T> b = gload8(dout + off);
 #pragma unroll
@@ -162,10 +163,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Rows of Q and K hold dg <= D elements, rows of V and dO dvg <= DV (each
     // a multiple of 8); the columns past them are zeros in registers and
     // LDS, so they add nothing to any product.
-    const T* qh = q + bh * (long)n * dg;
-    const T* kh = k + bh * (long)m * dg;
-    const T* vh = v + bh * (long)m * dvg;
-    const T* oh = dout + bh * (long)n * dvg;
+    const HeadView hq = head_view(si, bh, n, dg), hk = head_view(si, bh, m, dg);
+    const HeadView hv = head_view(si, bh, m, dvg), ho = head_view(si, bh, n, dvg);
+    const T* qh = q + hq.base;
+    const T* kh = k + hk.base;
+    const T* vh = v + hv.base;
+    const T* oh = dout + ho.base;
     const float* lh = lse2 + bh * (long)n_pad;
     const float* dh = Dw + bh * (long)n_pad;
 
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // P only reach dK and dV rows that are written as zeros).
     {
         TileLoader<D, C::BN, NW> ldK;
-        ldK.init(wave, lane, dg);
-        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)mb * dg * 2), j0, wave);
+        ldK.init(wave, lane, dg, hk.stride);
+        tile_fill<D, C::BN, NW>(ldK, sK, make_rsrc(kh, (uint32_t)mb * hk.stride * 2), j0, wave);
     }
     // This lane's V row for key tile kt (key kw0 + 32 kt + li): B operand of
     // dP = dO V^T.
@@ -185,7 +188,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc)
             vreg[kt][kc] = (key < mb && 16 * kc + 8 * g < dvg)
-                               ? gload8(vh + (long)key * dvg + 16 * kc + 8 * g) : vec8<T>{};
+                               ? gload8(vh + (long)key * hv.stride + 16 * kc + 8 * g)
+                               : vec8<T>{};
     }
 
     TileOffsets<D> toQ;
@@ -211,14 +215,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Query tile i0 into a buffer: Q and dO rows (rows past nb come back as
     // zeros; their LSE2 is +inf, so P = 0 and they contribute nothing), and
     // the per-row LSE2 and D.
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)nb * dg * 2);
-    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)nb * dvg * 2);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(qh, (uint32_t)nb * hq.stride * 2);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(oh, (uint32_t)nb * ho.stride * 2);
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(lh, (uint32_t)n_pad * 4);
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(dh, (uint32_t)n_pad * 4);
     TileLoader<D, BM, NW> ldQ;
-    ldQ.init(wave, lane, dg);
+    ldQ.init(wave, lane, dg, hq.stride);
     TileLoader<DV, BM, NW> ldO;
-    ldO.init(wave, lane, dvg);
+    ldO.init(wave, lane, dvg, ho.stride);
     auto stage = [&](auto buf_, int i0) __attribute__((always_inline)) {
         tile_fill<D, BM, NW>(ldQ, pick(buf_, sQ0, sQ1), rQ, i0, wave);
         tile_fill<DV, BM, NW>(ldO, pick(buf_, sO0, sO1), rO, i0, wave);
@@ -391,8 +395,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Accumulator slot vv of tile (kt, x) holds key kw0 + 32kt + 8(vv>>2) +
     // 4g + (vv&3), column 32x + li.  Keys past mb are padding: zeros.
-    T* dkh = dk + bh * (long)m * dg;
-    T* dvh = dvo + bh * (long)m * dvg;
+    T* dkh = dk + hk.base;
+    T* dvh = dvo + hv.base;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -406,12 +410,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
                 for (int x = 0; x < D / 32; ++x)
                     if (32 * x + li < dg)
-                        dkh[(long)key * dg + 32 * x + li] =
+                        dkh[(long)key * hk.stride + 32 * x + li] =
                             real ? (T)(accK[kt][x][vv] * scale) : (T)0.f;
 #pragma unroll
                 for (int x = 0; x < DV / 32; ++x)
                     if (32 * x + li < dvg)
-                        dvh[(long)key * dvg + 32 * x + li] = real ? (T)accV[kt][x][vv] : (T)0.f;
+                        dvh[(long)key * hv.stride + 32 * x + li] =
+                            real ? (T)accV[kt][x][vv] : (T)0.f;
             }
         }
     }

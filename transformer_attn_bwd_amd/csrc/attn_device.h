@@ -179,30 +179,32 @@ __device__ __forceinline__ vec8<T> tile_read_tr_at(const T* tile, const TileOffs
 }
 
 // Element offset that lies past the end of every buffer the kernels read
-// (their byte ranges stay below 2^30): a buffer load there returns zeros.
+// (the C ABI keeps each head's byte range within 2^30): a buffer load there
+// returns zeros.
 constexpr int kPastEnd = 0x3ff00000;
 
 // Per-lane source offsets for filling a ROWS x C tile with NW waves from a
-// row-major matrix whose rows hold G <= C elements (G a multiple of 8),
-// computed once: load jj of wave w fills kilobyte ii = w + NW*jj of the
-// tile, this lane fetching chunk c = s ^ swz(r) of tile row r (p = 64 ii +
-// lane, r = p / CPR, s = p % CPR); off[jj] is that chunk's element offset
-// from the tile's first global row, or kPastEnd for chunks c >= G/8, which
-// then fill with zeros (a narrower head is padded to the tile width).
+// matrix whose rows hold `width` <= C elements (a multiple of 8) and start
+// `stride` elements apart, computed once: load jj of wave w fills kilobyte
+// ii = w + NW*jj of the tile, this lane fetching chunk c = s ^ swz(r) of
+// tile row r (p = 64 ii + lane, r = p / CPR, s = p % CPR); off[jj] is that
+// chunk's element offset from the tile's first global row, or kPastEnd for
+// chunks c >= width/8, which then fill with zeros (a narrower head is
+// padded to the tile width).
 template <int C, int ROWS, int NW>
 struct TileLoader {
     using T = SwzTile<C>;
     static constexpr int N = ROWS * T::CPR / 64 / NW;
     static_assert(N * 64 * NW == ROWS * T::CPR, "tile loads must split evenly over the waves");
     int off[N];
-    int G;     // elements per global row
-    __device__ __forceinline__ void init(int w, int lane, int g_width = C) {
-        G = g_width;
+    int stride;   // elements from one global row to the next
+    __device__ __forceinline__ void init(int w, int lane, int width = C, int row_stride = 0) {
+        stride = row_stride > 0 ? row_stride : width;
 #pragma unroll
         for (int jj = 0; jj < N; ++jj) {
             const int p = (w + NW * jj) * 64 + lane;
             const int r = p / T::CPR, c = (p % T::CPR) ^ T::swz(r);
-            off[jj] = 8 * c < G ? r * G + 8 * c : kPastEnd;
+            off[jj] = 8 * c < width ? r * stride + 8 * c : kPastEnd;
         }
     }
 };
@@ -215,9 +217,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              0x00020000);
 }
 
-// Fill a tile from rows row0 .. row0 + ROWS - 1 of the [*, G] T matrix
-// behind `rsrc` (buffer loads straight into LDS); rows past the end of the
-// buffer, and columns G .. C-1, come back as zeros.
+// Fill a tile from rows row0 .. row0 + ROWS - 1 of the T matrix behind
+// `rsrc` (buffer loads straight into LDS); rows past the end of the
+// buffer, and columns width .. C-1, come back as zeros.
 template <int C, int ROWS, int NW, typename T>
 __device__ __forceinline__ void tile_fill(const TileLoader<C, ROWS, NW>& L, T* lds_tile,
                                           __amdgpu_buffer_rsrc_t rsrc, int row0, int w) {
@@ -225,7 +227,7 @@ __device__ __forceinline__ void tile_fill(const TileLoader<C, ROWS, NW>& L, T* l
     for (int jj = 0; jj < TileLoader<C, ROWS, NW>::N; ++jj)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (ATTN_LDS void*)(lds_tile + (w + NW * jj) * 512),
                                                  16, (unsigned)(2 * L.off[jj]),
-                                                 (unsigned)(2 * row0 * L.G), 0, 0);
+                                                 (unsigned)(2 * row0 * L.stride), 0, 0);
 }
 
 __device__ __forceinline__ float xor_lane32(float x) {

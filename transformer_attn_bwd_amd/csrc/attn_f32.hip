@@ -63,22 +63,24 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     const long bh = blockIdx.y;
     if (i >= n) return;
     const SeqLens len = seq_lens(si, bh, n, m);
-    const float* kh = k + bh * (long)m * d;
-    const float* vh = v + bh * (long)m * dv;
+    const HeadView hq = head_view(si, bh, n, d), hk = head_view(si, bh, m, d);
+    const HeadView hv = head_view(si, bh, m, dv), ho = head_view(si, bh, n, dv);
+    const float* kh = k + hk.base;
+    const float* vh = v + hv.base;
     RowVec qi, acc;
-    qi.load(q + (bh * (long)n + i) * d, d, lane);
+    qi.load(q + hq.base + (long)i * hq.stride, d, lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc.x[e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
     int jend = causal ? min(i + len.off + 1, len.m) : len.m;
     if (i >= len.n) jend = 0;
     for (int j = 0; j < jend; ++j) {
-        const float s = qi.dot(kh + (long)j * d, d, lane) * scale;
+        const float s = qi.dot(kh + (long)j * hk.stride, d, lane) * scale;
         const float m_new = fmaxf(m_run, s);
         const float alpha = expf(m_run - m_new);
         const float p = expf(s - m_new);
         l_run = l_run * alpha + p;
-        const float* vj = vh + (long)j * dv;
+        const float* vj = vh + (long)j * hv.stride;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int c = lane + 64 * e;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
         m_run = m_new;
     }
     const bool seen = jend > 0;
-    acc.store(o + (bh * (long)n + i) * dv, dv, lane, seen ? 1.f / l_run : 0.f);
+    acc.store(o + ho.base + (long)i * ho.stride, dv, lane, seen ? 1.f / l_run : 0.f);
     if (lane == 0) lse[bh * (long)n + i] = seen ? m_run + logf(l_run) : -INFINITY;
 }
 
@@ -105,8 +107,9 @@ __global__ __launch_bounds__(256) void preprocess_f32_kernel(
     const int nb = seq_lens(si, bh, n, 1).n;
     float acc = 0.f, l = -INFINITY;
     if (i < nb) {
-        const float* orow = o + (bh * (long)n + i) * dv;
-        const float* drow = dout + (bh * (long)n + i) * dv;
+        const HeadView ho = head_view(si, bh, n, dv);
+        const float* orow = o + ho.base + (long)i * ho.stride;
+        const float* drow = dout + ho.base + (long)i * ho.stride;
         for (int c = 0; c < dv; ++c) acc += orow[c] * drow[c];
         l = lse[bh * (long)n + i];
     }
@@ -125,17 +128,19 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(
     const long bh = blockIdx.y;
     if (j >= m) return;
     const SeqLens len = seq_lens(si, bh, n, m);
-    const float* qh = q + bh * (long)n * d;
-    const float* oh = dout + bh * (long)n * dv;
+    const HeadView hq = head_view(si, bh, n, d), hk = head_view(si, bh, m, d);
+    const HeadView hv = head_view(si, bh, m, dv), ho = head_view(si, bh, n, dv);
+    const float* qh = q + hq.base;
+    const float* oh = dout + ho.base;
     RowVec kj, vj, gk, gv;
-    kj.load(k + (bh * (long)m + j) * d, d, lane);
-    vj.load(v + (bh * (long)m + j) * dv, dv, lane);
+    kj.load(k + hk.base + (long)j * hk.stride, d, lane);
+    vj.load(v + hv.base + (long)j * hv.stride, dv, lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) gk.x[e] = gv.x[e] = 0.f;
     const int iend = j < len.m ? len.n : 0;
     for (int i = causal ? max(j - len.off, 0) : 0; i < iend; ++i) {
-        const float* qi = qh + (long)i * d;
-        const float* doi = oh + (long)i * dv;
+        const float* qi = qh + (long)i * hq.stride;
+        const float* doi = oh + (long)i * ho.stride;
         const float s = kj.dot(qi, d, lane) * scale;
         const float p = expf(s - lse_ws[bh * (long)n_pad + i]);
         const float dp = vj.dot(doi, dv, lane);
@@ -147,8 +152,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(
             if (c < dv) gv.x[e] += p * doi[c];
         }
     }
-    gk.store(dk + (bh * (long)m + j) * d, d, lane, scale);
-    gv.store(dvo + (bh * (long)m + j) * dv, dv, lane, 1.f);
+    gk.store(dk + hk.base + (long)j * hk.stride, d, lane, scale);
+    gv.store(dvo + hv.base + (long)j * hv.stride, dv, lane, 1.f);
 }
 
 // One wave per query row i: dQ_i = scale sum_j dS_ij K_j.
@@ -162,11 +167,13 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(
     const long bh = blockIdx.y;
     if (i >= n) return;
     const SeqLens len = seq_lens(si, bh, n, m);
-    const float* kh = k + bh * (long)m * d;
-    const float* vh = v + bh * (long)m * dv;
+    const HeadView hq = head_view(si, bh, n, d), hk = head_view(si, bh, m, d);
+    const HeadView hv = head_view(si, bh, m, dv), ho = head_view(si, bh, n, dv);
+    const float* kh = k + hk.base;
+    const float* vh = v + hv.base;
     RowVec qi, doi, g;
-    qi.load(q + (bh * (long)n + i) * d, d, lane);
-    doi.load(dout + (bh * (long)n + i) * dv, dv, lane);
+    qi.load(q + hq.base + (long)i * hq.stride, d, lane);
+    doi.load(dout + ho.base + (long)i * ho.stride, dv, lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) g.x[e] = 0.f;
     const float li = lse_ws[bh * (long)n_pad + i];
@@ -174,10 +181,10 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(
     int jend = causal ? min(i + len.off + 1, len.m) : len.m;
     if (i >= len.n || li == INFINITY) jend = 0;
     for (int j = 0; j < jend; ++j) {
-        const float* kj = kh + (long)j * d;
+        const float* kj = kh + (long)j * hk.stride;
         const float s = qi.dot(kj, d, lane) * scale;
         const float p = expf(s - li);
-        const float dp = doi.dot(vh + (long)j * dv, dv, lane);
+        const float dp = doi.dot(vh + (long)j * hv.stride, dv, lane);
         const float ds = p * (dp - Di);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(
             if (c < d) g.x[e] += ds * kj[c];
         }
     }
-    g.store(dq + (bh * (long)n + i) * d, d, lane, scale);
+    g.store(dq + hq.base + (long)i * hq.stride, d, lane, scale);
 }
 
 }  // namespace

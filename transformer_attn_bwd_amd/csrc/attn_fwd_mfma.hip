@@ -67,9 +67,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Rows of Q and K hold dg <= D elements, rows of V and O dvg <= DV (each
     // a multiple of 8); the columns past them are zeros in registers and
     // LDS, so they add nothing to any product.
-    const T* qh = q + bh * (long)n * dg;
-    const T* kh = k + bh * (long)m * dg;
-    const T* vh = v + bh * (long)m * dvg;
+    const HeadView hq = head_view(si, bh, n, dg), hk = head_view(si, bh, m, dg);
+    const HeadView hv = head_view(si, bh, m, dvg), ho = head_view(si, bh, n, dvg);
+    const T* qh = q + hq.base;
+    const T* kh = k + hk.base;
+    const T* vh = v + hv.base;
 
     // A negative scale is handled by negating Q, so that the row max of
     // S * c2 is c2 times the row max of the computed S.
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int kc = 0; kc < KA; ++kc) {
             const bool in = ok && 16 * kc + 8 * g < dg;
-            vec8<T> x = in ? gload8(qh + (long)myq[t] * dg + 16 * kc + 8 * g) : vec8<T>{};
+            vec8<T> x = in ? gload8(qh + (long)myq[t] * hq.stride + 16 * kc + 8 * g) : vec8<T>{};
             if (neg) x = __builtin_bit_cast(vec8<T>, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
             qreg[t][kc] = x;
             // keep the Q operands in AGPRs (MFMAs read them from there), so
@@ -111,12 +113,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     // Key tiles go to LDS buffer s & 1 for step s, fetched one step ahead;
     // rows past mb come back as zeros and are masked.
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * dg * 2);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * dvg * 2);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kh, (uint32_t)mb * hk.stride * 2);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vh, (uint32_t)mb * hv.stride * 2);
     TileLoader<D, BN, NW> ldK;
-    ldK.init(wave, lane, dg);
+    ldK.init(wave, lane, dg, hk.stride);
     TileLoader<DV, BN, NW> ldV;
-    ldV.init(wave, lane, dvg);
+    ldV.init(wave, lane, dvg, hv.stride);
     auto stage = [&](auto buf_, int k0) __attribute__((always_inline)) {
         tile_fill<D, BN, NW>(ldK, pick(buf_, sK0, sK1), rK, k0, wave);
         tile_fill<DV, BN, NW>(ldV, pick(buf_, sV0, sV1), rV, k0, wave);
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const bool seen = myq[t] < nb && l_tot > 0.f;
         const float inv = seen ? 1.f / l_tot : 0.f;
         if (myq[t] < n) {
-            T* orow = o + (bh * (long)n + myq[t]) * dvg;
+            T* orow = o + ho.base + (long)myq[t] * ho.stride;
 #pragma unroll
             for (int x = 0; x < NXV; ++x) {
 #pragma unroll

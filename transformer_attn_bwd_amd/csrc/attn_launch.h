@@ -25,6 +25,7 @@ struct Problem {
     int dtype = 0;
     const int* seqlens_q = nullptr;         // device [B] or null (n for every b)
     const int* seqlens_k = nullptr;         // device [B] or null (m for every b)
+    bool bshd = false;                      // tensors [B, seq, H, dim] instead of [B, H, seq, dim]
     long heads() const { return B * H; }
 };
 
@@ -37,16 +38,32 @@ inline int mfma_widths(const Problem& p) {
     return (td && tv) ? (td << 8) | tv : 0;
 }
 
-// What the kernels need to find a head's lengths and causal offset.
+// What the kernels need to find a head's rows, lengths and causal offset.
 struct SeqInfo {
     const int* sq;     // per-batch query lengths or null
     const int* sk;     // per-batch key lengths or null
     int H;             // heads per batch element (blockIdx.x / H is the batch)
     int br;            // 1: causal diagonal aligned bottom-right
+    int bshd;          // 1: tensors are [B, seq, H, dim], else [B, H, seq, dim]
 };
 
 inline SeqInfo seq_info(const Problem& p) {
-    return {p.seqlens_q, p.seqlens_k, (int)p.H, p.mask == kMaskCausalBottomRight ? 1 : 0};
+    return {p.seqlens_q, p.seqlens_k, (int)p.H, p.mask == kMaskCausalBottomRight ? 1 : 0,
+            p.bshd ? 1 : 0};
+}
+
+// Where head bh's rows live in a tensor with `rows` rows of `width`
+// elements per head: element offset of its row 0, and the distance between
+// consecutive rows.  [B, H, seq, dim]: the head is one contiguous block;
+// [B, seq, H, dim]: rows of the H heads interleave.
+struct HeadView {
+    long base;
+    int stride;
+};
+__device__ __forceinline__ HeadView head_view(const SeqInfo& si, long bh, int rows, int width) {
+    if (!si.bshd) return {bh * (long)rows * width, width};
+    const int b = (int)bh / si.H, h = (int)bh - b * si.H;
+    return {((long)b * rows * si.H + h) * width, si.H * width};
 }
 
 // Lengths of head bh: n_b query rows and m_b key rows take part (values
