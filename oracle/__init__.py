@@ -259,3 +259,34 @@ def attn_bwd_masked(q, k, v, dout, scale=None, mask="none", seqlens_q=None, seql
     if rc:
         raise ValueError("oracle_attn_bwd_masked: invalid sizes or mask")
     return out
+
+
+# ---------------------------------------------------------------- projections
+#
+# The layer around attention (eulerpad "Attention backward" Problems 7 and
+# 10; datatweets "Step 4: Back to the Parameters and Input"): for tokens
+# t = 1..T (batch and sequence flattened), X [T, d_model], Q = X W_Q,
+# K = X W_K, V = X W_V with W_Q, W_K [d_model, H d] and W_V [d_model, H dv]
+# holding the heads side by side (columns (h-1) d + 1 .. h d belong to head
+# h), and Y = O_cat W_O with O_cat [T, H dv] the heads' outputs side by side
+# and W_O [H dv, d_model].  Plain float64 matrix products of the stated
+# formulas; the weights' gradients sum over every token.
+
+
+def out_proj_bwd(o_cat, g, w_o):
+    """Problem 10: for Y = O_cat W_O and G = dL/dY, dW_O = O_cat^T G and
+    dL/dO_cat = G W_O^T (whose column block h is head h's dO).
+    o_cat [T, H dv], g [T, d_model], w_o [H dv, d_model]."""
+    o_cat, g, w_o = _f64(o_cat), _f64(g), _f64(w_o)
+    return {"dw_o": o_cat.T @ g, "do_cat": g @ w_o.T}
+
+
+def in_proj_bwd(x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat):
+    """Problem 7: dW_Q = X^T dQ, dW_K = X^T dK, dW_V = X^T dV and
+    dX = dQ W_Q^T + dK W_K^T + dV W_V^T (X feeds all three projections, so
+    the three paths add).  x [T, d_model]; dq_cat, dk_cat [T, H d];
+    dv_cat [T, H dv]."""
+    x, w_q, w_k, w_v = (_f64(t) for t in (x, w_q, w_k, w_v))
+    dq, dk, dv = (_f64(t) for t in (dq_cat, dk_cat, dv_cat))
+    return {"dw_q": x.T @ dq, "dw_k": x.T @ dk, "dw_v": x.T @ dv,
+            "dx": dq @ w_q.T + dk @ w_k.T + dv @ w_v.T}

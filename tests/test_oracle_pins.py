@@ -80,13 +80,13 @@ def test_toy_head_projection_gradients_match_fd():
     t = _toy_head()
     X, Wq, Wk, Wv, G = t["X"], t["Wq"], t["Wk"], t["Wv"], t["G"]
     r = oracle.attn_bwd(X @ Wq, X @ Wk, X @ Wv, G, scale=1.0 / np.sqrt(8))
-    dQ, dK, dV = r["dq"], r["dk"], r["dv"]
-    XT = X.transpose(0, 2, 1)
-    analytic = {
-        "dWq": np.sum(XT @ dQ, axis=0), "dWk": np.sum(XT @ dK, axis=0),
-        "dWv": np.sum(XT @ dV, axis=0),
-        "dX": dQ @ Wq.T + dK @ Wk.T + dV @ Wv.T,
-    }
+    # the projection gradients from the oracle's in_proj_bwd, tokens of the
+    # two batch items flattened into rows
+    T = X.shape[0] * X.shape[1]
+    p = oracle.in_proj_bwd(X.reshape(T, -1), Wq, Wk, Wv, r["dq"].reshape(T, -1),
+                           r["dk"].reshape(T, -1), r["dv"].reshape(T, -1))
+    analytic = {"dWq": p["dw_q"], "dWk": p["dw_k"], "dWv": p["dw_v"],
+                "dX": p["dx"].reshape(X.shape)}
     eps = pr["fd_eps"]
     params = {"dWq": "Wq", "dWk": "Wk", "dWv": "Wv", "dX": "X"}
     for gname, pname in params.items():
