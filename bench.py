@@ -9,7 +9,13 @@ as context.  FLOPs follow the convention 2nm(3d + 2dv) per head (10nmd when
 d = dv), halved for causal.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (N must be 1)
---workload NAME --no-cpu-baseline --cpu-heads H.
+--workload NAME --no-cpu-baseline --cpu-heads H --no-proj.
+
+Beside the backward, "layer_proj" times the projection gradients of the
+multi-head layer around it at the workload's sizes (T = B n tokens,
+d_model = H d): attn_out_proj_bwd (dW_O, dO_cat) and attn_in_proj_bwd
+(dW_Q, dW_K, dW_V, dX), 2 T d_model (2 H dv + 2 H d + H dv) x 2 flop, and
+the same products through torch.matmul for context.
 """
 from __future__ import annotations
 
@@ -103,6 +109,50 @@ def time_loop(fn, steps, torch, warmup=0):
     return start.elapsed_time(end) / steps
 
 
+def proj_flops(T, dm, hd, hdv) -> float:
+    # dW_O and dO_cat: 2 T dm hdv each; dW_Q, dW_K, dW_V: 2 T dm (2 hd + hdv);
+    # dX: 2 T dm (2 hd + hdv)
+    return 2.0 * T * dm * (2 * hdv + 2 * (2 * hd + hdv))
+
+
+def proj_bench(w, steps, torch, attn):
+    """Projection gradients at the workload's layer sizes (synthetic
+    16-bit inputs on the GPU)."""
+    T, hd, hdv = w.B * w.n, w.H * w.d, w.H * w.dv
+    dm = hd
+    dev = "cuda:0"
+    dt = w.torch_dtype
+    g = torch.Generator(device=dev).manual_seed(9)
+    r = lambda *shape: torch.randn(shape, generator=g, device=dev).to(dt)
+    X, G, o_cat = r(T, dm), r(T, dm), r(T, hdv)
+    Wq, Wk, Wv, Wo = r(dm, hd), r(dm, hd), r(dm, hdv), r(hdv, dm)
+    dQ, dK, dV = r(T, hd), r(T, hd), r(T, hdv)
+    dw_o, do_cat = attn.out_proj_bwd(o_cat, G, Wo)
+    grads = attn.in_proj_bwd(X, Wq, Wk, Wv, dQ, dK, dV)
+    out_ms = time_loop(lambda: attn.out_proj_bwd(o_cat, G, Wo, dw_o=dw_o, do_cat=do_cat),
+                       steps, torch, 3)
+    in_ms = time_loop(lambda: attn.in_proj_bwd(X, Wq, Wk, Wv, dQ, dK, dV, out=grads),
+                      steps, torch, 3)
+
+    def torch_products():
+        torch.matmul(o_cat.t(), G)
+        torch.matmul(G, Wo.t())
+        for dP in (dQ, dK, dV):
+            torch.matmul(X.t(), dP)
+        torch.matmul(dQ, Wq.t()).add_(torch.matmul(dK, Wk.t())).add_(torch.matmul(dV, Wv.t()))
+
+    ref_ms = time_loop(torch_products, steps, torch, 3)
+    f = proj_flops(T, dm, hd, hdv)
+    ms = out_ms + in_ms
+    return {
+        "T": T, "d_model": dm, "hd": hd, "hdv": hdv, "flops": f,
+        "out_proj_ms": round(out_ms, 4), "in_proj_ms": round(in_ms, 4),
+        "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+        "pct_of_peak": round(100.0 * f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "torch_matmul_ms": round(ref_ms, 4),
+    }
+
+
 def cpu_baseline(w, inputs, heads_wanted):
     """The float64 oracle's backward on a bounded sample of the workload's
     heads, on the host cores; reported in the metric's unit."""
@@ -134,6 +184,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0)
+    ap.add_argument("--no-proj", action="store_true", help="skip the projection-gradient timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (a known-traffic "
                          "reference for hardware byte counters)")
@@ -243,6 +294,9 @@ def main():
         "outputs_finite": ok,
         "wall_s_timed": round(t_wall, 3),
     }
+    if not args.no_proj and w.dtype != "fp32":
+        print("bench: projection gradients ...", file=sys.stderr, flush=True)
+        result["layer_proj"] = proj_bench(w, max(5, args.steps // 2), torch, attn)
     if not args.no_cpu_baseline and w.dtype != "fp32":
         print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inputs_cpu, args.cpu_heads)

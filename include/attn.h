@@ -165,6 +165,42 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 int layout, int dtype, int flags, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * Projection gradients of the multi-head self-attention layer around the
+ * attention (eulerpad "Attention backward" Problems 7 and 10; datatweets
+ * "Step 4").  Tokens are rows, T = B * n; with ATTN_LAYOUT_BSHD the
+ * attention tensors [B, n, H, dim] are exactly these [T, H * dim] matrices,
+ * so the calls chain without copies:
+ *
+ *   attn_out_proj_bwd -> do_cat -> attn_bwd_ex (BSHD) -> dq, dk, dv -> attn_in_proj_bwd
+ *
+ * dtype ATTN_BF16 or ATTN_F16 (16-bit products, float32 accumulation);
+ * weight gradients are written in float32, the others in dtype.  Sizes:
+ * T >= 0; d_model, hd = H*d and hdv = H*dv multiples of 8, at least 8;
+ * every matrix at most 2^30 bytes.  Rows are contiguous (row stride = row
+ * length); 16-byte aligned pointers.  Validation and streams as for
+ * attn_fwd.  Nothing is allocated.
+ *
+ * attn_out_proj_bwd: for Y = O_cat W_O with o_cat [T, hdv], w_o
+ * [hdv, d_model] and g = dL/dY [T, d_model], writes dw_o = o_cat^T g
+ * [hdv, d_model] and do_cat = g w_o^T [T, hdv] (its column block h is head
+ * h's dL/dO).
+ */
+int attn_out_proj_bwd(const void* o_cat, const void* g, const void* w_o, float* dw_o,
+                      void* do_cat, int T, int d_model, int hdv, int dtype, void* stream);
+
+/*
+ * attn_in_proj_bwd: for Q = X W_Q, K = X W_K, V = X W_V with x [T, d_model],
+ * w_q, w_k [d_model, hd], w_v [d_model, hdv] and the attention gradients
+ * dq_cat, dk_cat [T, hd], dv_cat [T, hdv], writes dw_q = x^T dq_cat,
+ * dw_k = x^T dk_cat ([d_model, hd]), dw_v = x^T dv_cat ([d_model, hdv]) and
+ * dx = dq_cat w_q^T + dk_cat w_k^T + dv_cat w_v^T ([T, d_model]).
+ */
+int attn_in_proj_bwd(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                     const void* dq_cat, const void* dk_cat, const void* dv_cat, float* dw_q,
+                     float* dw_k, float* dw_v, void* dx, int T, int d_model, int hd, int hdv,
+                     int dtype, void* stream);
+
 /* Static string naming a status code. */
 const char* attn_status_str(int status);
 

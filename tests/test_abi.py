@@ -216,3 +216,37 @@ def test_layout_constants_match_header():
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     vals = dict((k.strip(), int(v)) for k, v in (e.split("=") for e in body.split(",") if "=" in e))
     assert vals == {"ATTN_LAYOUT_BHSD": B.ATTN_LAYOUT_BHSD, "ATTN_LAYOUT_BSHD": B.ATTN_LAYOUT_BSHD}
+
+
+def _outp(lib, T=64, dm=64, hdv=64, dtype=B.ATTN_BF16, ptrs=None):
+    p = ptrs if ptrs is not None else [FAKE] * 5
+    return lib.attn_out_proj_bwd(*p, T, dm, hdv, dtype, NULL)
+
+
+def _inp(lib, T=64, dm=64, hd=64, hdv=64, dtype=B.ATTN_BF16, ptrs=None):
+    p = ptrs if ptrs is not None else [FAKE] * 11
+    return lib.attn_in_proj_bwd(*p, T, dm, hd, hdv, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=B.ATTN_F32), B.ATTN_EUNSUPPORTED),
+    (dict(T=-1), B.ATTN_EINVAL),
+    (dict(dm=0), B.ATTN_EINVAL),
+    (dict(dm=60), B.ATTN_EUNSUPPORTED),          # rows must be whole 16-byte chunks
+    (dict(hdv=100), B.ATTN_EUNSUPPORTED),
+    (dict(T=1 << 20, dm=1024), B.ATTN_EUNSUPPORTED),   # a matrix over 2^30 bytes
+])
+def test_proj_rejects(lib, kw, code):
+    assert _outp(lib, **kw) == code
+    assert _inp(lib, **kw) == code
+
+
+def test_proj_null_and_misaligned(lib):
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = NULL
+        assert _outp(lib, ptrs=p) == B.ATTN_EINVAL
+    for i in range(11):
+        p = [FAKE] * 11
+        p[i] = ctypes.c_void_p((1 << 20) + 8)
+        assert _inp(lib, ptrs=p) == B.ATTN_EINVAL

@@ -31,7 +31,7 @@ DQ_MODES = {"auto": ATTN_DQ_AUTO, "separate": ATTN_DQ_SEPARATE}
 STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
-            "attn_status_str", "attn_version")
+            "attn_out_proj_bwd", "attn_in_proj_bwd", "attn_status_str", "attn_version")
 
 _lib = None
 
@@ -62,6 +62,10 @@ def load():
     lib.attn_fwd_ex.restype = I
     lib.attn_bwd_ex.argtypes = [vp] * 11 + [I] * 6 + [F, I, I, I, I, vp, Z, vp]
     lib.attn_bwd_ex.restype = I
+    lib.attn_out_proj_bwd.argtypes = [vp] * 5 + [I] * 4 + [vp]
+    lib.attn_out_proj_bwd.restype = I
+    lib.attn_in_proj_bwd.argtypes = [vp] * 11 + [I] * 5 + [vp]
+    lib.attn_in_proj_bwd.restype = I
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -216,3 +220,62 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     if st != ATTN_OK:
         raise AttnError(st, where)
     return dq, dk, dv
+
+
+def _mat(t, rows, cols, name):
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} must be [{rows}, {cols}], got {tuple(t.shape)}")
+    _check_dev(t)
+
+
+def out_proj_bwd(o_cat, g, w_o, dw_o=None, do_cat=None):
+    """(dW_O, dO_cat) for Y = O_cat W_O and G = dL/dY: dW_O = O_cat^T G
+    (float32 [H dv, d_model]) and dO_cat = G W_O^T (dtype, [T, H dv]).
+    o_cat [T, H dv], g [T, d_model], w_o [H dv, d_model]; a [B, n, H, dv]
+    attention output viewed as [T, H dv] is o_cat."""
+    lib = load()
+    T, hdv = o_cat.shape
+    dm = g.shape[1]
+    _mat(o_cat, T, hdv, "o_cat")
+    _mat(g, T, dm, "g")
+    _mat(w_o, hdv, dm, "w_o")
+    if g.dtype != o_cat.dtype or w_o.dtype != o_cat.dtype:
+        raise TypeError("o_cat, g and w_o must share a dtype")
+    dw_o = torch.empty((hdv, dm), dtype=torch.float32, device=g.device) if dw_o is None else dw_o
+    do_cat = torch.empty((T, hdv), dtype=g.dtype, device=g.device) if do_cat is None else do_cat
+    _mat(dw_o, hdv, dm, "dw_o")
+    _mat(do_cat, T, hdv, "do_cat")
+    st = lib.attn_out_proj_bwd(_ptr(o_cat), _ptr(g), _ptr(w_o), _ptr(dw_o), _ptr(do_cat), T, dm,
+                               hdv, _dtype_code(g), _stream(g))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_out_proj_bwd")
+    return dw_o, do_cat
+
+
+def in_proj_bwd(x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat, out=None):
+    """dW_Q, dW_K, dW_V (float32) and dX (dtype) for Q = X W_Q, K = X W_K,
+    V = X W_V: a dict with keys dw_q, dw_k, dw_v, dx.  x [T, d_model],
+    w_q, w_k [d_model, H d], w_v [d_model, H dv]; dq_cat, dk_cat [T, H d],
+    dv_cat [T, H dv] (attention gradients in [B, n, H, dim] viewed as 2-d)."""
+    lib = load()
+    T, dm = x.shape
+    hd, hdv = w_q.shape[1], w_v.shape[1]
+    for t, r, c, name in ((x, T, dm, "x"), (w_q, dm, hd, "w_q"), (w_k, dm, hd, "w_k"),
+                          (w_v, dm, hdv, "w_v"), (dq_cat, T, hd, "dq_cat"),
+                          (dk_cat, T, hd, "dk_cat"), (dv_cat, T, hdv, "dv_cat")):
+        _mat(t, r, c, name)
+        if t.dtype != x.dtype:
+            raise TypeError("all inputs must share a dtype")
+    dev = x.device
+    o = dict(out or {})
+    o.setdefault("dw_q", torch.empty((dm, hd), dtype=torch.float32, device=dev))
+    o.setdefault("dw_k", torch.empty((dm, hd), dtype=torch.float32, device=dev))
+    o.setdefault("dw_v", torch.empty((dm, hdv), dtype=torch.float32, device=dev))
+    o.setdefault("dx", torch.empty((T, dm), dtype=x.dtype, device=dev))
+    st = lib.attn_in_proj_bwd(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(dq_cat),
+                              _ptr(dk_cat), _ptr(dv_cat), _ptr(o["dw_q"]), _ptr(o["dw_k"]),
+                              _ptr(o["dw_v"]), _ptr(o["dx"]), T, dm, hd, hdv, _dtype_code(x),
+                              _stream(x))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_in_proj_bwd")
+    return o

@@ -20,7 +20,8 @@ OBJ_DIR = os.path.join(ROOT, "_build")
 # (source, element type or None): the MFMA kernel files are compiled once per
 # 16-bit element type, so that the slow instantiations build in parallel.
 ELEMS = ("bf16", "f16")
-MFMA_SOURCES = ["attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip"]
+MFMA_SOURCES = ["attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip",
+                "attn_proj_gemm.hip"]
 SOURCES = ["attn_api.hip", "attn_f32.hip", *MFMA_SOURCES]
 UNITS = [("attn_api.hip", None), ("attn_f32.hip", None)] + [
     (src, elem) for src in MFMA_SOURCES for elem in ELEMS]

@@ -94,6 +94,29 @@ int hip_status() {
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+// Sizes of the projection calls: T >= 0, widths multiples of 8 (16-byte
+// rows), every matrix within 2^30 bytes (32-bit buffer offsets).
+int check_proj(int T, int d_model, int hd, int hdv, int dtype, attn::ProjProblem* p) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_EUNSUPPORTED;
+    if (T < 0 || d_model < 8 || hd < 8 || hdv < 8) return ATTN_EINVAL;
+    if (d_model % 8 || hd % 8 || hdv % 8) return ATTN_EUNSUPPORTED;
+    const long widest = d_model > hd ? (d_model > hdv ? d_model : hdv) : (hd > hdv ? hd : hdv);
+    const long rows = T > d_model ? T : d_model;
+    if (rows * widest * 2 > (1L << 30) || (long)hd * d_model * 4 > (1L << 30) ||
+        (long)hdv * d_model * 4 > (1L << 30))
+        return ATTN_EUNSUPPORTED;
+    p->T = T;
+    p->d_model = d_model;
+    p->hd = hd;
+    p->hdv = hdv;
+    return ATTN_OK;
+}
+
+bool mat_ok(const void* p, long elems, size_t align) {
+    if (elems == 0) return true;
+    return p != nullptr && aligned(p, align);
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +250,49 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     return ATTN_OK;
+}
+
+int attn_out_proj_bwd(const void* o_cat, const void* g, const void* w_o, float* dw_o,
+                      void* do_cat, int T, int d_model, int hdv, int dtype, void* stream) {
+    attn::ProjProblem p;
+    int st = check_proj(T, d_model, 8, hdv, dtype, &p);
+    if (st != ATTN_OK) return st;
+    const long t = T;
+    if (!mat_ok(o_cat, t * hdv, 16) || !mat_ok(g, t * d_model, 16) ||
+        !mat_ok(w_o, (long)hdv * d_model, 16) || !mat_ok(dw_o, (long)hdv * d_model, 16) ||
+        !mat_ok(do_cat, t * hdv, 16))
+        return ATTN_EINVAL;
+    (void)hipGetLastError();
+    if (dtype == ATTN_BF16)
+        attn::launch_out_proj_bwd<__bf16>(p, o_cat, g, w_o, dw_o, do_cat, (hipStream_t)stream);
+    else
+        attn::launch_out_proj_bwd<_Float16>(p, o_cat, g, w_o, dw_o, do_cat, (hipStream_t)stream);
+    return hip_status();
+}
+
+int attn_in_proj_bwd(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                     const void* dq_cat, const void* dk_cat, const void* dv_cat, float* dw_q,
+                     float* dw_k, float* dw_v, void* dx, int T, int d_model, int hd, int hdv,
+                     int dtype, void* stream) {
+    attn::ProjProblem p;
+    int st = check_proj(T, d_model, hd, hdv, dtype, &p);
+    if (st != ATTN_OK) return st;
+    const long t = T, dm = d_model;
+    if (!mat_ok(x, t * dm, 16) || !mat_ok(w_q, dm * hd, 16) || !mat_ok(w_k, dm * hd, 16) ||
+        !mat_ok(w_v, dm * hdv, 16) || !mat_ok(dq_cat, t * hd, 16) ||
+        !mat_ok(dk_cat, t * hd, 16) || !mat_ok(dv_cat, t * hdv, 16) ||
+        !mat_ok(dw_q, dm * hd, 16) || !mat_ok(dw_k, dm * hd, 16) ||
+        !mat_ok(dw_v, dm * hdv, 16) || !mat_ok(dx, t * dm, 16))
+        return ATTN_EINVAL;
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == ATTN_BF16)
+        attn::launch_in_proj_bwd<__bf16>(p, x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat, dw_q, dw_k,
+                                         dw_v, dx, s);
+    else
+        attn::launch_in_proj_bwd<_Float16>(p, x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat, dw_q,
+                                           dw_k, dw_v, dx, s);
+    return hip_status();
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -108,6 +108,21 @@ template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const Workspace& w, void* dq, hipStream_t s);
 
+// Projection gradients around attention (tokens as rows, T = B n):
+// matrices X [T, d_model], W_Q, W_K [d_model, hd], W_V [d_model, hdv],
+// W_O [hdv, d_model] with hd = H d, hdv = H dv.
+struct ProjProblem {
+    int T = 0, d_model = 0, hd = 0, hdv = 0;
+};
+template <typename T>
+void launch_out_proj_bwd(const ProjProblem& p, const void* o_cat, const void* g, const void* w_o,
+                         float* dw_o, void* do_cat, hipStream_t s);
+template <typename T>
+void launch_in_proj_bwd(const ProjProblem& p, const void* x, const void* w_q, const void* w_k,
+                        const void* w_v, const void* dq_cat, const void* dk_cat,
+                        const void* dv_cat, float* dw_q, float* dw_k, float* dw_v, void* dx,
+                        hipStream_t s);
+
 // fp32 path (one wave per row; any d, dv in 1..128).
 bool launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v, float* o,
                     float* lse, hipStream_t s);
