@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip", "attn_device.h", "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "81c9fcc9375f87e83b1f130e5f71bb6c83c7ab68fb1fe5d6f1242059d908acf0",
-    "bytes": {"bwd_dkdv": 7.745e+08, "bwd_dq": 6.432e+08},
+    "sources_sha256": "5fe1b0d17750f6f09f41c28624fc505feafe99e7130d729e91bd95be8878ef0a",
+    "bytes": {"bwd_dkdv": 7.437e+08, "bwd_dq": 6.167e+08},
 }
 
 

@@ -65,16 +65,17 @@ template <typename OutT>
 __device__ __forceinline__ void store_block(OutT* c, long ldc, int M, int N, int row0, int col0,
                                             f32x16 (&acc)[4][4], int g, int li) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    OutT* base = c + (long)(row0 + 4 * g) * ldc + col0 + li;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = col0 + 32 * j + li;
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * i + 8 * (v >> 2) + (v & 3);   // row - row0 - 4g
+            if (row0 + 4 * g + r >= M) continue;
+            OutT* rowp = base + (long)r * ldc;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-                if (row < M && col < N) c[(long)row * ldc + col] = (OutT)acc[i][j][v];
-            }
+            for (int j = 0; j < 4; ++j)
+                if (col0 + 32 * j + li < N) rowp[32 * j] = (OutT)acc[i][j][v];
         }
     }
 }
