@@ -109,6 +109,19 @@ def time_loop(fn, steps, torch, warmup=0):
     return start.elapsed_time(end) / steps
 
 
+def step_times(fn, steps, torch):
+    """Per-step durations (ms) from an event pair around each step."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
 def proj_flops(T, dm, hd, hdv) -> float:
     # dW_O and dO_cat: 2 T dm hdv each; dW_Q, dW_K, dW_V: 2 T dm (2 hd + hdv);
     # dX: 2 T dm (2 hd + hdv)
@@ -240,6 +253,8 @@ def main():
     t_wall = time.perf_counter() - t_wall
     print(f"bench: {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     ok = bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
+    # the spread of single steps (L2 not flushed between steps)
+    per_step = step_times(bwd_step, args.steps, torch)
 
     # per-kernel average launch durations (HIP events on the launch stream)
     kern_ms = {
@@ -267,6 +282,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
