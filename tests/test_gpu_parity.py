@@ -61,6 +61,9 @@ BF16_SHAPES = [
     _w("bf16_causal_700_d128", 1, 2, 700, 700, 128, 128, "bf16", True, 31),
     _w("bf16_cross_600x900_d128_dv64", 1, 1, 600, 900, 128, 64, "bf16", False, 32),
     _w("bf16_causal_520_d64", 2, 1, 520, 520, 64, 64, "bf16", True, 33),
+    # many heads: grids of 512 workgroups and more, several per compute unit
+    _w("bf16_4wave_causal_300_d128", 4, 64, 300, 300, 128, 128, "bf16", True, 36),
+    _w("bf16_4wave_cross_260x530_d64", 2, 128, 260, 530, 64, 64, "bf16", False, 37),
     # scale signs the kernels treat specially: negative (the forward negates
     # Q) and zero (uniform P over the visible keys)
     _w("bf16_negative_scale", 1, 1, 100, 150, 128, 128, "bf16", False, 34, 1.0, -0.1),
