@@ -296,7 +296,9 @@ def main():
         "flops_per_step": flops,
         "kernels_ms": {k_: round(v_, 4) for k_, v_ in kern_ms.items()},
         "fwd": {"ms": round(fwd_ms, 4),
-                "tflops": round(fwd_flops(w) / (fwd_ms * 1e-3) / 1e12, 2)},
+                "tflops": round(fwd_flops(w) / (fwd_ms * 1e-3) / 1e12, 2),
+                "pct_of_peak": round(100.0 * fwd_flops(w) / (fwd_ms * 1e-3) / 1e12
+                                     / PEAK_BF16_TFLOPS, 2)},
         "roofline": {
             "kernel": f"bwd_{dominant}",
             "bound": "mfma",

@@ -219,3 +219,41 @@ def test_error_leaves_outputs_untouched():
     assert ei.value.status == 4
     torch.cuda.synchronize()
     assert torch.all(dq == 3.0)
+
+
+def test_stages_compose_to_the_whole_backward():
+    """Running the preprocess, dK/dV and dQ kernels as three calls (the
+    timing flags) gives the bits of one call."""
+    w = _w("stages", 2, 2, 300, 300, 128, 128, "bf16", True, 42)
+    q, k, v, do = make_inputs(w, "cuda:0")
+    o, lse = attn.fwd(q, k, v, causal=True)
+    ws = torch.empty(attn.bwd_workspace_bytes(2, 2, 300, 300, 128, 128), dtype=torch.uint8,
+                     device="cuda:0")
+    whole = attn.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)
+    parts = [torch.full_like(t, 5.0) for t in (q, k, v)]
+    for stage in ("preprocess", "dkdv", "dq"):
+        attn.bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=parts[0], dk=parts[1],
+                 dv=parts[2], stages=[stage])
+    torch.cuda.synchronize()
+    for a, b in zip(whole, parts):
+        assert torch.equal(a, b)
+
+
+def test_determinism_fp16_masked_bshd():
+    """No atomics anywhere: repeated calls with lengths, the bottom-right
+    mask and the [B, seq, H, dim] layout give identical bits."""
+    dev = "cuda:0"
+    g = torch.Generator().manual_seed(43)
+    q, k, v, do = (torch.randn((3, 200, 2, 64), generator=g).to(torch.float16).to(dev)
+                   for _ in range(4))
+    sq = torch.tensor([200, 150, 7], dtype=torch.int32, device=dev)
+    sk = torch.tensor([180, 200, 30], dtype=torch.int32, device=dev)
+    kw = dict(mask="causal_bottom_right", seqlens_q=sq, seqlens_k=sk, layout="bshd")
+    o1, l1 = attn.fwd(q, k, v, **kw)
+    o2, l2 = attn.fwd(q, k, v, **kw)
+    a = attn.bwd(q, k, v, o1, do, l1, **kw)
+    b = attn.bwd(q, k, v, o1, do, l1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
