@@ -18,7 +18,8 @@
 // The running max is raised lazily: the accumulators and the row sum are
 // rescaled only when some row's max grows by more than 2^8 (in the base-2
 // domain), so P = exp2(S * scale * log2e - m) stays below 2^8 and the
-// rescale, which touches every accumulator, is rare.
+// rescale, which touches every accumulator, is rare; so is the exchange of
+// the two lanes' maxima that a rescale needs.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -172,25 +173,35 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         auto visible = [&](int kh, int e, int t) __attribute__((always_inline)) {
             return 32 * kh + 8 * (e >> 2) + (e & 3) <= lim[t];
         };
+        // The row max is only needed when it grows past the threshold, and
+        // it grows past it exactly when this lane's half of the keys or the
+        // other lane's half does: each lane tests its own half, and only
+        // when some lane of the wave sees growth are the halves exchanged
+        // (a round trip through LDS) and the running max raised.
         auto softmax_head = [&]() __attribute__((always_inline)) {
-            float m_new[2];
+            float mx[2];
             bool grow = false;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                float mx = -INFINITY;
+                mx[t] = -INFINITY;
 #pragma unroll
                 for (int kh = 0; kh < NKH; ++kh) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        if constexpr (MASKED) mx = visible(kh, e, t) ? fmaxf(mx, S[kh][t][e]) : mx;
-                        else mx = fmaxf(mx, S[kh][t][e]);
+                        if constexpr (MASKED)
+                            mx[t] = visible(kh, e, t) ? fmaxf(mx[t], S[kh][t][e]) : mx[t];
+                        else mx[t] = fmaxf(mx[t], S[kh][t][e]);
                     }
                 }
-                mx = fmaxf(mx, xor_lane32(mx));
-                m_new[t] = mx == -INFINITY ? m_run[t] : fmaxf(m_run[t], mx * cs);
-                grow |= m_new[t] > m_run[t] + kRescaleThreshold;
+                grow |= mx[t] != -INFINITY && mx[t] * cs > m_run[t] + kRescaleThreshold;
             }
             if (__any(grow)) {
+                float m_new[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float m2 = fmaxf(mx[t], xor_lane32(mx[t]));
+                    m_new[t] = m2 == -INFINITY ? m_run[t] : fmaxf(m_run[t], m2 * cs);
+                }
                 asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
