@@ -257,3 +257,21 @@ def test_determinism_fp16_masked_bshd():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_side_stream_matches_default_stream():
+    """Work is enqueued on the caller's current stream: the same call on a
+    side stream (default priority) gives the same bits once synchronised."""
+    w = _w("stream", 1, 2, 260, 260, 64, 64, "bf16", True, 44)
+    q, k, v, do = make_inputs(w, "cuda:0")
+    o, lse = attn.fwd(q, k, v, causal=True)
+    ref = attn.bwd(q, k, v, o, do, lse, causal=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o2, lse2 = attn.fwd(q, k, v, causal=True)
+        got = attn.bwd(q, k, v, o2, do, lse2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
