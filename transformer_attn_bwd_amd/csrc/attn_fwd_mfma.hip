@@ -75,9 +75,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const T* vh = v + hv.base;
 
     // A negative scale is handled by negating Q, so that the row max of
-    // S * c2 is c2 times the row max of the computed S.
+    // S * c2 is c2 times the row max of the computed S.  A zero scale is
+    // raised to 1e-30, so that masked logits (-inf) stay -inf after the
+    // multiplication (-inf * 0 would be NaN); 1e-30 times a finite logit is
+    // far below float32 resolution at 1, so every visible weight is exactly
+    // 1, as with a zero scale.
     const bool neg = c2 < 0.f;
-    const float cs = neg ? -c2 : c2;
+    const float cs = fmaxf(neg ? -c2 : c2, 1e-30f);
 
     // Query tile t of this wave: rows i0 + (BM/2) t + 32 wave + (0..31), one
     // tile from each half of the workgroup's rows (even causal work).
@@ -125,8 +129,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         tile_fill<DV, BN, NW>(ldV, pick(buf_, sV0, sV1), rV, k0, wave);
     };
 
-    // O^T accumulators (AGPRs), running max (base 2) and this lane's part
-    // of the running sum, per query tile.
+    // O^T accumulators, running max (base 2) and this lane's part of the
+    // running sum, per query tile.  The accumulators stay in VGPRs: the
+    // rare rescale multiplies them in place, where AGPR accumulators made
+    // the compiler copy all 128 of them to VGPRs at the top of every step
+    // (about 7% of the kernel's time at 4k context).
     f32x16 acc[NXV][2];
 #pragma unroll
     for (int x = 0; x < NXV; ++x) {
@@ -170,6 +177,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if constexpr (CAUSAL) lim[t] = min(lim[t], myq[t] + off - k0 - 4 * g);
             }
         }
+        // Masked steps set the invisible logits to -inf once, before the
+        // row max; exp2 then gives their P = 0 with no second test (one
+        // compare per element, consumed at once, instead of 64 lane masks
+        // kept for the P pass, which spilled scalar registers).
         auto visible = [&](int kh, int e, int t) __attribute__((always_inline)) {
             return 32 * kh + 8 * (e >> 2) + (e & 3) <= lim[t];
         };
@@ -189,8 +200,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         if constexpr (MASKED)
-                            mx[t] = visible(kh, e, t) ? fmaxf(mx[t], S[kh][t][e]) : mx[t];
-                        else mx[t] = fmaxf(mx[t], S[kh][t][e]);
+                            S[kh][t][e] = visible(kh, e, t) ? S[kh][t][e] : -INFINITY;
+                        mx[t] = fmaxf(mx[t], S[kh][t][e]);
                     }
                 }
                 grow |= mx[t] != -INFINITY && mx[t] * cs > m_run[t] + kRescaleThreshold;
@@ -202,7 +213,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     const float m2 = fmaxf(mx[t], xor_lane32(mx[t]));
                     m_new[t] = m2 == -INFINITY ? m_run[t] : fmaxf(m_run[t], m2 * cs);
                 }
-                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const float alpha = m_new[t] == m_run[t] ? 1.f : fast_exp2(m_run[t] - m_new[t]);
@@ -222,7 +232,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 float pv = fast_exp2(__builtin_fmaf(S[kh][t][e0 + s], cs, -mbase[t]));
-                if constexpr (MASKED) pv = visible(kh, e0 + s, t) ? pv : 0.f;
                 p8[s] = pv;
                 l_run[t] += pv;
             }
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 constexpr int cx = f - NKH * KA, c = cx / NXV, x = cx % NXV;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    mfma32_agpr(cur, Pb[c][t], acc[x][t]);
+                    acc[x][t] = mfma32(cur, Pb[c][t], acc[x][t]);
                 });
                 // chunk c + 1 while the products of chunk c run
                 if constexpr (c + 1 < NC && x == 0)
@@ -295,10 +304,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         do_step(B1{}, MaskOn{}, s + 1);
     }
     if (s < nsteps) do_step(B0{}, MaskOn{}, s);
-
-    // wait states between the last MFMA writing an accumulator and the
-    // reads below
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // Accumulator slot vv of tile (x, t) holds column 32x + 8(vv>>2) + 4g +
     // (vv&3) of query myq[t]; the row sum is split over this lane and the
