@@ -37,10 +37,11 @@ def _inputs(B, H, n, m, d, dv, dtype, seed, lq, lk, mult=1.0):
     return q, k, v, do
 
 
-def _run(case, layout="bhsd"):
+def _run(case, layout="bhsd", scale=None):
     (name, B, H, n, m, d, dv, dtype, mask, lq, lk, seed) = case
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
     say(f"case {name}: B={B} H={H} n={n} m={m} d={d} dv={dv} {dtype} mask={mask} lq={lq} "
-        f"lk={lk} layout={layout}")
+        f"lk={lk} layout={layout} scale={scale}")
     q, k, v, do = _inputs(B, H, n, m, d, dv, dtype, seed, lq, lk)
     dev = "cuda:0"
     # [B, seq, H, dim] copies for the bshd layout; results are viewed back
@@ -51,7 +52,6 @@ def _run(case, layout="bhsd"):
     qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
     sq = torch.tensor(lq, dtype=torch.int32, device=dev) if lq is not None else None
     sk = torch.tensor(lk, dtype=torch.int32, device=dev) if lk is not None else None
-    scale = 1.0 / np.sqrt(d)
     o, lse = attn.fwd(qd, kd, vd, scale=scale, mask=mask, seqlens_q=sq, seqlens_k=sk,
                       layout=layout)
     dq, dk, dvv = attn.bwd(qd, kd, vd, o, dod, lse, scale=scale, mask=mask, seqlens_q=sq,
@@ -113,6 +113,25 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_masked_parity(case):
     _run(case)
+
+
+SCALE_CASES = [
+    (("zero_scale_br_varlen", 3, 2, 300, 400, 128, 128, "bf16", "causal_bottom_right",
+      [300, 120, 77], [400, 64, 200], 150), 0.0),
+    (("zero_scale_topleft_fp16", 2, 1, 257, 257, 64, 64, "fp16", "causal", [257, 100],
+      [257, 130], 151), 0.0),
+    (("negative_scale_br_varlen", 2, 2, 333, 257, 128, 64, "bf16", "causal_bottom_right",
+      [333, 90], [257, 200], 152), -0.07),
+]
+
+
+@pytest.mark.parametrize("case,scale", SCALE_CASES,
+                         ids=lambda c: c[0] if isinstance(c, tuple) else str(c))
+def test_masked_zero_and_negative_scale(case, scale):
+    """Masks and lengths with a zero scale (every visible weight equal: the
+    forward must keep masked and padded logits at -inf, not -inf * 0) and a
+    negative one (the forward negates Q)."""
+    _run(case, scale=scale)
 
 
 BSHD_CASES = [
