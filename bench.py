@@ -261,6 +261,10 @@ def main():
         "preprocess": time_loop(lambda: bwd_step(["preprocess"]), args.steps, torch, 3),
         "dkdv": time_loop(lambda: bwd_step(["dkdv"]), args.steps, torch, 3),
         "dq": time_loop(lambda: bwd_step(["dq"]), args.steps, torch, 3),
+        # what a whole 16-bit backward launches first: the dQ pass with the
+        # preprocess in its prologue
+        "dq_with_preprocess": time_loop(lambda: bwd_step(["preprocess", "dq"]), args.steps,
+                                        torch, 3),
     }
     fwd_ms = time_loop(fwd_step, args.steps, torch, 3)
     # restore outputs of a whole backward after the single-stage runs

@@ -94,9 +94,12 @@ enum attn_bwd_flags {
     ATTN_DQ_AUTO = 0,         /* library's choice (currently ATTN_DQ_SEPARATE) */
     ATTN_DQ_SEPARATE = 1,     /* a second pass per query tile recomputes P and dS:
                                  deterministic, no atomics */
-    /* Bits 8-10 restrict which kernels run (0 = all, in this order).  They
-       exist so that each kernel can be timed on its own; a caller wanting
-       gradients leaves them 0.  Later stages read what earlier ones wrote. */
+    /* Bits 8-10 restrict which kernels run (0 = all).  They exist so that
+       each kernel can be timed on its own; a caller wanting gradients
+       leaves them 0.  Later stages read what earlier ones wrote (the
+       preprocess before the other two).  A 16-bit call that includes both
+       the preprocess and dQ does the preprocess inside the dQ pass, which
+       then runs before dK/dV; the results are the same bits either way. */
     ATTN_STAGE_PREPROCESS = 1 << 8,   /* D = rowsum(dO o O), LSE rescale */
     ATTN_STAGE_DKDV = 1 << 9,         /* dK and dV */
     ATTN_STAGE_DQ = 1 << 10           /* dQ */

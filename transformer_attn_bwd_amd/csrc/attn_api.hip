@@ -221,8 +221,20 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     (void)hipGetLastError();
 
     const bool bf = is_16bit(dtype);
+    // 16-bit calls that run both the preprocess and the dQ pass fold the
+    // former into the latter's prologue (same bits), which then runs before
+    // the dK/dV kernel that reads its results.
+    const bool fused =
+        bf && n > 0 && (stages & ATTN_STAGE_PREPROCESS) && (stages & ATTN_STAGE_DQ);
     bool ok = true;
-    if (n > 0 && (stages & ATTN_STAGE_PREPROCESS)) {
+    if (fused) {
+        ok = dtype == ATTN_BF16
+                 ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, o, lse, w, dq, s)
+                 : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, o, lse, w, dq, s);
+        if (!ok) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (n > 0 && (stages & ATTN_STAGE_PREPROCESS) && !fused) {
         ok = bf ? (dtype == ATTN_BF16
                        ? attn::launch_bwd_preprocess_mfma<__bf16>(p, o, dout, lse, w, s)
                        : attn::launch_bwd_preprocess_mfma<_Float16>(p, o, dout, lse, w, s))
@@ -240,10 +252,12 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((st = hip_status()) != ATTN_OK) return st;
     }
-    if (n > 0 && (stages & ATTN_STAGE_DQ)) {
+    if (n > 0 && (stages & ATTN_STAGE_DQ) && !fused) {
         ok = bf ? (dtype == ATTN_BF16
-                       ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, w, dq, s)
-                       : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, w, dq, s))
+                       ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, nullptr, nullptr,
+                                                          w, dq, s)
+                       : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, nullptr, nullptr,
+                                                            w, dq, s))
                 : attn::launch_bwd_dq_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                           (const float*)dout, w, (float*)dq, s);
         if (!ok) return ATTN_EUNSUPPORTED;

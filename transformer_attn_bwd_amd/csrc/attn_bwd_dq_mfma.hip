@@ -20,6 +20,11 @@
 // AGPRs.  The causal mask (S_ij = -inf for
 // j > i, i.e. P_ij = 0, eulerpad P8) is applied only in key tiles that
 // reach past the workgroup's first query.
+//
+// Given O and the forward's LSE, the pass also does the preprocess for its
+// own rows (D = rowsum(dO o O), LSE in base 2) in its prologue and writes
+// them to the workspace for the dK/dV kernel that follows, which saves the
+// separate preprocess launch and its second read of dO.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -37,9 +42,9 @@ struct DqCfg {
 template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ Dw, T* __restrict__ dq, int n, int m, int dg, int dvg, int n_pad,
-    float scale, float c2, SeqInfo si) {
+    const T* __restrict__ dout, float* __restrict__ lse2, float* __restrict__ Dw,
+    const T* __restrict__ o, const float* __restrict__ lse, T* __restrict__ dq, int n, int m,
+    int dg, int dvg, int n_pad, float scale, float c2, SeqInfo si) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     // One LDS variable per buffer: the compiler can then tell that reads
@@ -105,8 +110,49 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         for (int kc = 0; kc < D / 16; ++kc) asm volatile("" : "+a"(qreg[t][kc]));
 #pragma unroll
         for (int kc = 0; kc < DV / 16; ++kc) asm volatile("" : "+a"(oreg[t][kc]));
-        l2[t] = ok ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
-        Dq[t] = ok ? Dw[bh * (long)n_pad + myq[t]] : 0.f;
+        if (o == nullptr) {
+            l2[t] = ok ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
+            Dq[t] = ok ? Dw[bh * (long)n_pad + myq[t]] : 0.f;
+        }
+    }
+    if (o != nullptr) {
+        // The preprocess for this workgroup's rows, in the arithmetic order
+        // of bwd_preprocess_kernel, so that both give the same bits: each
+        // 8-column chunk c summed in order, then the chunks pairwise at
+        // distances 8, 4, 2, 1 (16 chunks; 4, 2, 1 for 8).  This lane holds
+        // the chunks c = 2 kc + g, so the last step is the exchange with the
+        // lane 32 away.  Rows past nb get D = 0 and LSE2 = +inf, rows that
+        // saw no key (LSE = -inf) LSE2 = +inf.
+        const HeadView hov = head_view(si, bh, n, dvg);
+        const T* orow0 = o + hov.base;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bool ok = myq[t] < nb;
+            float sc[DV / 16];
+#pragma unroll
+            for (int kc = 0; kc < DV / 16; ++kc) {
+                const bool in = ok && 16 * kc + 8 * g < dvg;
+                const vec8<T> a =
+                    in ? gload8(orow0 + (long)myq[t] * hov.stride + 16 * kc + 8 * g) : vec8<T>{};
+                const vec8<T> b = oreg[t][kc];
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+                sc[kc] = acc;
+            }
+#pragma unroll
+            for (int w = DV / 32; w >= 1; w /= 2) {
+#pragma unroll
+                for (int kc = 0; kc < w; ++kc) sc[kc] = sc[kc] + sc[kc + w];
+            }
+            Dq[t] = sc[0] + xor_lane32(sc[0]);
+            const float l = ok ? lse[bh * (long)n + myq[t]] : -INFINITY;
+            l2[t] = l > -INFINITY ? l * kLog2e : INFINITY;
+            if (g == 0 && myq[t] < n_pad) {
+                lse2[bh * (long)n_pad + myq[t]] = l2[t];
+                Dw[bh * (long)n_pad + myq[t]] = Dq[t];
+            }
+        }
     }
 
     TileOffsets<D> toK;
@@ -307,31 +353,32 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
 template <typename T, int D, int DV>
 void launch_dq(const Problem& p, const void* q, const void* k, const void* v, const void* dout,
-               const Workspace& w, void* dq, hipStream_t s) {
+               const void* o, const float* lse, const Workspace& w, void* dq, hipStream_t s) {
     using C = DqCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
     const SeqInfo si = seq_info(p);
     if (p.causal)
         bwd_dq_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
-            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D, (const T*)o,
+            lse, (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
     else
         bwd_dq_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
-            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+            (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D, (const T*)o,
+            lse, (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
 }
 
 }  // namespace
 
 template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
-                        const void* dout, const Workspace& w, void* dq, hipStream_t s) {
+                        const void* dout, const void* o, const float* lse, const Workspace& w,
+                        void* dq, hipStream_t s) {
     switch (mfma_widths(p)) {
-    case 0x4040: launch_dq<T, 64, 64>(p, q, k, v, dout, w, dq, s); break;
-    case 0x4080: launch_dq<T, 64, 128>(p, q, k, v, dout, w, dq, s); break;
-    case 0x8040: launch_dq<T, 128, 64>(p, q, k, v, dout, w, dq, s); break;
-    case 0x8080: launch_dq<T, 128, 128>(p, q, k, v, dout, w, dq, s); break;
+    case 0x4040: launch_dq<T, 64, 64>(p, q, k, v, dout, o, lse, w, dq, s); break;
+    case 0x4080: launch_dq<T, 64, 128>(p, q, k, v, dout, o, lse, w, dq, s); break;
+    case 0x8040: launch_dq<T, 128, 64>(p, q, k, v, dout, o, lse, w, dq, s); break;
+    case 0x8080: launch_dq<T, 128, 128>(p, q, k, v, dout, o, lse, w, dq, s); break;
     default: return false;
     }
     return true;
@@ -343,7 +390,7 @@ bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const vo
 #error "compile once per element type: -DATTN_ELEM=bf16 or -DATTN_ELEM=f16"
 #endif
 template bool launch_bwd_dq_mfma<ATTN_ELEM>(const Problem&, const void*, const void*,
-                                           const void*, const void*, const Workspace&, void*,
-                                           hipStream_t);
+                                           const void*, const void*, const void*, const float*,
+                                           const Workspace&, void*, hipStream_t);
 
 }  // namespace attn

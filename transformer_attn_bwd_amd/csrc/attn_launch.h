@@ -104,9 +104,13 @@ template <typename T>
 bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const void* v,
                           const void* dout, const Workspace& w, void* dk, void* dv,
                           hipStream_t s);
+// With o and lse non-null the dQ pass also does the preprocess for its rows
+// (same bits as launch_bwd_preprocess_mfma) and writes it to w; with them
+// null it reads w.
 template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
-                        const void* dout, const Workspace& w, void* dq, hipStream_t s);
+                        const void* dout, const void* o, const float* lse, const Workspace& w,
+                        void* dq, hipStream_t s);
 
 // Projection gradients around attention (tokens as rows, T = B n):
 // matrices X [T, d_model], W_Q, W_K [d_model, hd], W_V [d_model, hdv],
