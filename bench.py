@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the backward kernels on causal_4k_d128, from
+# HBM bytes per launch of the dK/dV kernel (the dominant one) on causal_4k_d128, from
 # rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the
 # same counters read for a plain 1 GiB device copy (x2.0 and x1.0).  They
 # hold only for the kernel sources they were taken on, identified by hash;
@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip", "attn_device.h", "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "5fe1b0d17750f6f09f41c28624fc505feafe99e7130d729e91bd95be8878ef0a",
-    "bytes": {"bwd_dkdv": 7.483e+08, "bwd_dq": 6.166e+08},
+    "sources_sha256": "32c915f19f7b476f0e6aed18ce332fe14eb8e58f92c2b1fd989dff5a919206dc",
+    "bytes": {"bwd_dkdv": 7.427e+08},
 }
 
 
