@@ -221,22 +221,54 @@ def test_error_leaves_outputs_untouched():
     assert torch.all(dq == 3.0)
 
 
-def test_stages_compose_to_the_whole_backward():
+STAGE_CASES = [
+    # (name, B, H, n, m, d, dv, dtype, mask, lengths q, lengths k, layout, seed)
+    ("bf16_causal_d128", 2, 2, 300, 300, 128, 128, torch.bfloat16, "causal", None, None,
+     "bhsd", 42),
+    ("fp16_causal_d64", 2, 3, 257, 257, 64, 64, torch.float16, "causal", None, None, "bhsd", 44),
+    ("bf16_cross_d128_dv64", 1, 2, 200, 333, 128, 64, torch.bfloat16, "none", None, None,
+     "bhsd", 45),
+    ("bf16_varlen_br_d40_dv72_bshd", 3, 2, 300, 260, 40, 72, torch.bfloat16,
+     "causal_bottom_right", [300, 129, 5], [260, 200, 33], "bshd", 46),
+]
+
+
+@pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: c[0])
+def test_stages_compose_to_the_whole_backward(case):
     """Running the preprocess, dK/dV and dQ kernels as three calls (the
-    timing flags) gives the bits of one call."""
-    w = _w("stages", 2, 2, 300, 300, 128, 128, "bf16", True, 42)
-    q, k, v, do = make_inputs(w, "cuda:0")
-    o, lse = attn.fwd(q, k, v, causal=True)
-    ws = torch.empty(attn.bwd_workspace_bytes(2, 2, 300, 300, 128, 128), dtype=torch.uint8,
-                     device="cuda:0")
-    whole = attn.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)
+    timing flags) gives the bits of one call, in which the dQ pass does
+    the preprocess for its rows: the workspace (LSE in base 2 and D for
+    every padded row) and dQ, dK, dV are equal bit for bit.  The cases
+    cover both reduction shapes of D (64- and 128-wide tiles), a width
+    short of its tile, lengths, padded rows and the [B, seq, H, dim]
+    layout."""
+    name, B, H, n, m, d, dv, dt, mask, lq, lk, layout, seed = case
+    say(f"case stages {name}")
+    dev = "cuda:0"
+    g = torch.Generator().manual_seed(seed)
+    shp = (lambda rows, w: (B, rows, H, w)) if layout == "bshd" else \
+        (lambda rows, w: (B, H, rows, w))
+    q, k = (torch.randn(shp(r_, d), generator=g).to(dt).to(dev) for r_ in (n, m))
+    v = torch.randn(shp(m, dv), generator=g).to(dt).to(dev)
+    do = torch.randn(shp(n, dv), generator=g).to(dt).to(dev)
+    sq = torch.tensor(lq, dtype=torch.int32, device=dev) if lq else None
+    sk = torch.tensor(lk, dtype=torch.int32, device=dev) if lk else None
+    kw = dict(mask=mask, seqlens_q=sq, seqlens_k=sk, layout=layout)
+    o, lse = attn.fwd(q, k, v, **kw)
+    nbytes = attn.bwd_workspace_bytes(B, H, n, m, d, dv, dt)
+    n_pad = (n + 127) // 128 * 128
+    used = 2 * B * H * n_pad           # floats: LSE2 then D
+    ws1 = torch.full((nbytes,), 7, dtype=torch.uint8, device=dev)
+    ws2 = torch.full((nbytes,), 9, dtype=torch.uint8, device=dev)
+    whole = attn.bwd(q, k, v, o, do, lse, workspace=ws1, **kw)
     parts = [torch.full_like(t, 5.0) for t in (q, k, v)]
     for stage in ("preprocess", "dkdv", "dq"):
-        attn.bwd(q, k, v, o, do, lse, causal=True, workspace=ws, dq=parts[0], dk=parts[1],
-                 dv=parts[2], stages=[stage])
+        attn.bwd(q, k, v, o, do, lse, workspace=ws2, dq=parts[0], dk=parts[1], dv=parts[2],
+                 stages=[stage], **kw)
     torch.cuda.synchronize()
-    for a, b in zip(whole, parts):
-        assert torch.equal(a, b)
+    assert torch.equal(ws1[:4 * used], ws2[:4 * used])
+    for a_, b_ in zip(whole, parts):
+        assert torch.equal(a_, b_)
 
 
 def test_determinism_fp16_masked_bshd():

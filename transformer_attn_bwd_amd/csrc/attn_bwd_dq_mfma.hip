@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 const vec8<T> b = oreg[t][kc];
                 float acc = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
                 sc[kc] = acc;
             }
 #pragma unroll

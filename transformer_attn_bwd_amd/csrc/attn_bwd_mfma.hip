@@ -40,14 +40,17 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     const int i = valid_row ? (int)(row % n_pad) : 0;
     const int nb = seq_lens(si, bh, n, 1).n;
     float acc = 0.f;
-    // rows hold dvg <= DV elements; lanes past them add nothing
+    // rows hold dvg <= DV elements; lanes past them add nothing.  Explicit
+    // fused multiply-adds, one per element in order: the dQ pass repeats
+    // this sum and must get the same bits (left to itself the compiler pairs
+    // fp16 products into dot2 instructions here but not there).
     if (valid_row && i < nb && 8 * part < dvg) {
         const HeadView hv = head_view(si, bh, n, dvg);
         const long off = hv.base + (long)i * hv.stride + 8 * part;
         vec8<T> a = gload8(o + off);
         vec8<T> b = gload8(dout + off);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
