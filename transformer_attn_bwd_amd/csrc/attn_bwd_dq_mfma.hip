@@ -54,6 +54,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __shared__ __align__(1024) T sK1[BN * D];
     __shared__ __align__(1024) T sV0[BN * DV];
     __shared__ __align__(1024) T sV1[BN * DV];
+    // the epilogue's staging rows: 64 rows x 64 columns per wave
+    __shared__ __align__(1024) T sE[NW * 64 * 64];
     auto Kbuf = [&](auto b_) __attribute__((always_inline)) -> T* {
         if constexpr (decltype(b_)::value == 0) return sK0;
         else return sK1;
@@ -331,22 +333,38 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // reads below
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // Accumulator slot vv of tile (x, t) holds column d = 32x + 8(vv>>2) +
-    // 4g + (vv&3) of query myq[t].
+    // 4g + (vv&3) of query myq[t].  The tiles go out through this wave's
+    // staging rows in LDS, 64 columns at a time: written row-major (16-byte
+    // chunks XOR-swizzled by row), read back as whole rows and stored 16
+    // bytes per lane, eight 128-byte row segments per instruction.
+    T* reg = sE + wave * 64 * 64;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        if (myq[t] < n) {
-            T* qrow = dq + hq.base + (long)myq[t] * hq.stride;
+    for (int sl = 0; sl < D / 64; ++sl) {
 #pragma unroll
-            for (int x = 0; x < D / 32; ++x) {
+        for (int t = 0; t < 2; ++t) {
+            const int row = 32 * t + li;
+#pragma unroll
+            for (int xs = 0; xs < 2; ++xs) {
 #pragma unroll
                 for (int vq = 0; vq < 4; ++vq) {
                     vec4<T> w;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) w[r] = (T)(acc[x][t][4 * vq + r] * scale);
-                    const int col = 32 * x + 8 * vq + 4 * g;
-                    if (col < dg) *reinterpret_cast<vec4<T>*>(qrow + col) = w;
+                    for (int r = 0; r < 4; ++r)
+                        w[r] = (T)(acc[2 * sl + xs][t][4 * vq + r] * scale);
+                    const int chunk = 4 * xs + vq;
+                    *reinterpret_cast<vec4<T>*>(reg + row * 64 + 8 * (chunk ^ (row & 7)) + 4 * g) = w;
                 }
             }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int lin = 64 * i + lane, row = lin / 8, chunk = lin % 8;
+            const vec8<T> w8 =
+                *reinterpret_cast<const vec8<T>*>(reg + row * 64 + 8 * (chunk ^ (row & 7)));
+            const int query = i0 + (C::BM / 2) * (row / 32) + 32 * wave + row % 32;
+            const int col = 64 * sl + 8 * chunk;
+            if (query < n && col < dg)
+                *reinterpret_cast<vec8<T>*>(dq + hq.base + (long)query * hq.stride + col) = w8;
         }
     }
 }

@@ -78,8 +78,8 @@ struct DkdvCfg {
 // KB = DV/16, NX = D/32, NXV = DV/32 the step issues, in order,
 //   S    2KA MFMAs  j = 2r + kt          S[kt]  += Q_r  K[kt]_r^T
 //   dP   2KB MFMAs  j = 2KA + 2r + kt    dP[kt] += dO_r V[kt]_r^T
-//   dV  4NXV MFMAs  2(c NXV + x) + kt    dV[kt][x] += P[kt]^T_c dO_c,x
-//   dK  4NX  MFMAs  2(c NX + x) + kt     dK[kt][x] += dS[kt]^T_c Q_c,x
+//   dV  4NXV MFMAs  2(c NXV + x) + kt    dV[kt][x]^T += (dO_c,x)^T P[kt]_c
+//   dK  4NX  MFMAs  2(c NX + x) + kt     dK[kt][x]^T += (Q_c,x)^T dS[kt]_c
 // (kt: 32-key tile of the wave, r: 16-wide chunk of d or dv, c: 16-query
 // half of the step, x: 32-column block).  Operand fragments read from LDS:
 //   f <  KA               Q rows, chunk f              (first used by j = 2f)
@@ -126,7 +126,11 @@ struct DkdvSched {
 // in registers (B operands of S = Q K^T and dP = dO V^T, lane = key); the
 // query tiles (32 rows of Q and dO, with their LSE2 and D) stream through
 // two LDS buffers.  Each Q, dO, Q^T and dO^T fragment read from LDS feeds
-// two MFMAs (the wave's two key tiles).  dK and dV accumulate in AGPRs.
+// two MFMAs (the wave's two key tiles).  dK and dV accumulate, transposed,
+// in AGPRs: the A and B operands of a 32x32x16 MFMA have the same lane
+// layout, so swapping them yields the transposed product in the same
+// registers, and the transposed tiles hold four consecutive columns of one
+// key per lane group, which the epilogue needs.
 template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -345,10 +349,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 dP[kt] = mfma32(fr[SC::F_DO + r], vreg[kt][r], dP[kt]);
             } else if constexpr (j < SC::J_DK) {
                 constexpr int cx = (j - SC::J_DV) / 2, c = cx / SC::NXV, x = cx % SC::NXV;
-                mfma32_agpr(Pb[kt][c], fr[SC::F_DOT + cx], accV[kt][x]);
+                mfma32_agpr(fr[SC::F_DOT + cx], Pb[kt][c], accV[kt][x]);
             } else {
                 constexpr int cx = (j - SC::J_DK) / 2, c = cx / SC::NX, x = cx % SC::NX;
-                mfma32_agpr(dSb[kt][c], fr[SC::F_QT + cx], accK[kt][x]);
+                mfma32_agpr(fr[SC::F_QT + cx], dSb[kt][c], accK[kt][x]);
             }
             // softmax work of this slot
             static_for<32>([&](auto i_) {
@@ -396,33 +400,54 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // reads below
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // Accumulator slot vv of tile (kt, x) holds key kw0 + 32kt + 8(vv>>2) +
-    // 4g + (vv&3), column 32x + li.  Keys past mb are padding: zeros.
-    T* dkh = dk + hk.base;
-    T* dvh = dvo + hv.base;
+    // The products were taken with the operands swapped, so the
+    // accumulators hold dK^T and dV^T: slot vv of tile (kt, x) is column
+    // 32x + 8(vv>>2) + 4g + (vv&3) of key kw0 + 32kt + li.  They go out
+    // through this wave's 64 rows of the K tile in LDS (no other wave reads
+    // them, and the last step's barrier has passed): each slab of D columns
+    // is written there row-major (16-byte chunks XOR-swizzled by row), read
+    // back as whole rows and stored 16 bytes per lane, 1 KB of contiguous
+    // rows per instruction.  Keys past mb are padding: zeros.
+    T* reg = sK + C::KW * wave * D;
+    auto put_tile = [&](auto W_, const f32x16 (&acc)[2][W_.value / 32], int wcols, float mult,
+                        T* out, long stride) __attribute__((always_inline)) {
+        constexpr int W = decltype(W_)::value;
+        constexpr int SW = W < D ? W : D;      // slab width: what the region holds
+        constexpr int CH = SW / 8;             // 16-byte chunks per slab row
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+        for (int sl = 0; sl < W / SW; ++sl) {
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int key = kw0 + 32 * kt + 8 * (vv >> 2) + 4 * g + (vv & 3);
-            // (a padded key's accumulators may hold inf: S = 0 there, and P
-            // = exp2(-LSE2) overflows when a row's LSE is very negative, so
-            // its zeros are selected, not multiplied)
-            if (key < m) {
-                const bool real = key < mb;
+            for (int kt = 0; kt < 2; ++kt) {
+                const int row = 32 * kt + li;
+                const bool real = kw0 + row < mb;
 #pragma unroll
-                for (int x = 0; x < D / 32; ++x)
-                    if (32 * x + li < dg)
-                        dkh[(long)key * hk.stride + 32 * x + li] =
-                            real ? (T)(accK[kt][x][vv] * scale) : (T)0.f;
+                for (int xs = 0; xs < SW / 32; ++xs) {
+                    const int x = sl * (SW / 32) + xs;
 #pragma unroll
-                for (int x = 0; x < DV / 32; ++x)
-                    if (32 * x + li < dvg)
-                        dvh[(long)key * hv.stride + 32 * x + li] =
-                            real ? (T)accV[kt][x][vv] : (T)0.f;
+                    for (int vq = 0; vq < 4; ++vq) {
+                        vec4<T> w4;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            w4[r] = real ? (T)(acc[kt][x][4 * vq + r] * mult) : (T)0.f;
+                        const int chunk = 4 * xs + vq;
+                        *reinterpret_cast<vec4<T>*>(
+                            reg + row * SW + 8 * (chunk ^ (row & (CH - 1))) + 4 * g) = w4;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int lin = 64 * i + lane, row = lin / CH, chunk = lin % CH;
+                const vec8<T> w8 = *reinterpret_cast<const vec8<T>*>(
+                    reg + row * SW + 8 * (chunk ^ (row & (CH - 1))));
+                const int key = kw0 + row, col = sl * SW + 8 * chunk;
+                if (key < m && col < wcols)
+                    *reinterpret_cast<vec8<T>*>(out + (long)key * stride + col) = w8;
             }
         }
-    }
+    };
+    put_tile(std::integral_constant<int, D>{}, accK, dg, scale, dk + hk.base, hk.stride);
+    put_tile(std::integral_constant<int, DV>{}, accV, dvg, 1.f, dvo + hv.base, hv.stride);
 }
 
 template <typename T, int DV>

@@ -50,6 +50,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __shared__ __align__(1024) T sK1[BN * D];
     __shared__ __align__(1024) T sV0[BN * DV];
     __shared__ __align__(1024) T sV1[BN * DV];
+    // the epilogue's staging rows: 64 rows x 64 columns per wave
+    __shared__ __align__(1024) T sE[NW * 64 * 64];
     auto pick = [](auto b_, auto* x0, auto* x1) __attribute__((always_inline)) {
         if constexpr (decltype(b_)::value == 0) return x0;
         else return x1;
@@ -308,27 +310,47 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Accumulator slot vv of tile (x, t) holds column 32x + 8(vv>>2) + 4g +
     // (vv&3) of query myq[t]; the row sum is split over this lane and the
     // lane 32 away.  Rows past nb, and rows that see no key (row sum 0),
-    // are written as O = 0, LSE = -inf.
+    // are written as O = 0, LSE = -inf.  The O tiles go out through this
+    // wave's staging rows in LDS, 64 columns at a time: written row-major
+    // (16-byte chunks XOR-swizzled by row), read back as whole rows and
+    // stored 16 bytes per lane, eight 128-byte row segments per instruction.
+    float inv[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float l_tot = l_run[t] + xor_lane32(l_run[t]);
         const bool seen = myq[t] < nb && l_tot > 0.f;
-        const float inv = seen ? 1.f / l_tot : 0.f;
-        if (myq[t] < n) {
-            T* orow = o + ho.base + (long)myq[t] * ho.stride;
+        inv[t] = seen ? 1.f / l_tot : 0.f;
+        if (myq[t] < n && g == 0)
+            lse[bh * (long)n + myq[t]] = seen ? (m_run[t] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    T* reg = sE + wave * 64 * 64;
 #pragma unroll
-            for (int x = 0; x < NXV; ++x) {
+    for (int sl = 0; sl < DV / 64; ++sl) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = 32 * t + li;
+#pragma unroll
+            for (int xs = 0; xs < 2; ++xs) {
 #pragma unroll
                 for (int vq = 0; vq < 4; ++vq) {
                     vec4<T> w;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) w[r] = (T)(acc[x][t][4 * vq + r] * inv);
-                    const int col = 32 * x + 8 * vq + 4 * g;
-                    if (col < dvg) *reinterpret_cast<vec4<T>*>(orow + col) = w;
+                    for (int r = 0; r < 4; ++r)
+                        w[r] = (T)(acc[2 * sl + xs][t][4 * vq + r] * inv[t]);
+                    const int chunk = 4 * xs + vq;
+                    *reinterpret_cast<vec4<T>*>(reg + row * 64 + 8 * (chunk ^ (row & 7)) + 4 * g) = w;
                 }
             }
-            if (g == 0)
-                lse[bh * (long)n + myq[t]] = seen ? (m_run[t] + log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int lin = 64 * i + lane, row = lin / 8, chunk = lin % 8;
+            const vec8<T> w8 =
+                *reinterpret_cast<const vec8<T>*>(reg + row * 64 + 8 * (chunk ^ (row & 7)));
+            const int query = i0 + (C::BM / 2) * (row / 32) + 32 * wave + row % 32;
+            const int col = 64 * sl + 8 * chunk;
+            if (query < n && col < dvg)
+                *reinterpret_cast<vec8<T>*>(o + ho.base + (long)query * ho.stride + col) = w8;
         }
     }
 }
