@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip", "attn_device.h", "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "7055af104bde01cb0fc9c59da47092cfcd8f7ea083582969de9f82b85c9ca617",
-    "bytes": {"bwd_dkdv": 7.4210e+08},
+    "sources_sha256": "8ac4901f838bd2201c24e2a9bc95ad025c431533051902020ea13b58fb52e34a",
+    "bytes": {"bwd_dkdv": 7.6320e+08},
 }
 
 
