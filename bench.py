@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip", "attn_device.h", "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "8ac4901f838bd2201c24e2a9bc95ad025c431533051902020ea13b58fb52e34a",
+    "sources_sha256": "7c90c0964c97c6b56e87ff4d5dbbd003c3ec7c4e1d43dd39522444875db6bdac",
     "bytes": {"bwd_dkdv": 7.6320e+08},
 }
 

@@ -407,7 +407,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // them, and the last step's barrier has passed): each slab of D columns
     // is written there row-major (16-byte chunks XOR-swizzled by row), read
     // back as whole rows and stored 16 bytes per lane, 1 KB of contiguous
-    // rows per instruction.  Keys past mb are padding: zeros.
+    // rows per instruction.  Keys past mb are padding: zeros, selected rather
+    // than multiplied, since a padded key's accumulators may hold inf (S = 0
+    // there, and P = exp2(-LSE2) overflows when a row's LSE is very
+    // negative).
     T* reg = sK + C::KW * wave * D;
     auto put_tile = [&](auto W_, const f32x16 (&acc)[2][W_.value / 32], int wcols, float mult,
                         T* out, long stride) __attribute__((always_inline)) {
