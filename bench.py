@@ -204,8 +204,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each (batch, head) is independent; see the sharding notes in DESIGN.md)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each "
+              "(batch, head) is independent, so several GPUs would split the heads)",
               file=sys.stderr)
         sys.exit(2)
 
