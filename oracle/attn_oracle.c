@@ -6,10 +6,11 @@
  * CPU-baseline leg of the benchmark.  It shares no code, header, table or
  * helper with the HIP library.
  *
- * What it computes is the plain definition, one query row at a time ("every
- * formula is the row formula stacked", eulerpad "Attention backward", the
- * conventions before Problem 1).  For one head with Q (n x d), K (m x d),
- * V (m x dv) and upstream gradient dO (n x dv), and a scale s:
+ * What it computes is the plain definition, one query row at a time: each
+ * matrix formula is the per-row formula applied to every row (eulerpad
+ * "Attention backward", the conventions before Problem 1).  For one head
+ * with Q (n x d), K (m x d), V (m x dv) and upstream gradient dO (n x dv),
+ * and a scale s:
  *
  *   S_ij  = s * sum_l Q_il K_jl                 mlgrind "Forward"; eulerpad P1
  *   S_ij  = -inf for j > i when causal          mlgrind "Forward"; eulerpad P8
@@ -127,8 +128,8 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o
 }
 
 /*
- * Backward, full tensors, recomputing P from Q and K (mlgrind "Edge cases":
- * recompute P inside the backward pass).
+ * Backward, full tensors.  P is rebuilt from Q and K here rather than kept
+ * from the forward (mlgrind "Edge cases and conventions").
  *
  * Outputs (all required): dq [B,H,n,d], dk [B,H,m,d], dvv [B,H,m,dv],
  * Drow [B,H,n] = rowsum(dP o P), Drow_alt [B,H,n] = rowsum(dO o O),

@@ -250,3 +250,84 @@ def test_proj_null_and_misaligned(lib):
         p = [FAKE] * 11
         p[i] = ctypes.c_void_p((1 << 20) + 8)
         assert _inp(lib, ptrs=p) == B.ATTN_EINVAL
+
+
+# The binding sizes nothing itself: every tensor it passes on must have the
+# shape and dtype the library derives from q.  These checks run before the
+# device check, so CPU tensors exercise them here.
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def _bwd_args(**over):
+    import torch
+    a = dict(q=_t(1, 2, 8, 64), k=_t(1, 2, 16, 64), v=_t(1, 2, 16, 32), o=_t(1, 2, 8, 32),
+             do=_t(1, 2, 8, 32), lse=_t(1, 2, 8, dtype=torch.float32))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,exc", [
+    (dict(k=_t(1, 2, 16, 64, dtype=None).float()), TypeError),      # k dtype != q dtype
+    (dict(v=_t(1, 2, 16, 32).half()), TypeError),
+    (dict(o=_t(1, 2, 8, 64)), ValueError),                            # o width != dv
+    (dict(o=_t(1, 2, 8, 32).half()), TypeError),
+    (dict(do=_t(1, 2, 9, 32)), ValueError),                           # do rows != n
+    (dict(lse=_t(1, 2, 8)), TypeError),                               # lse must be float32
+    (dict(lse=_t(1, 2, 7).float()), ValueError),
+    (dict(dq=_t(1, 2, 8, 32)), ValueError),                           # dq must match q
+    (dict(dk=_t(1, 2, 16, 64).float()), TypeError),
+    (dict(dv=_t(1, 2, 15, 32)), ValueError),
+    (dict(workspace=_t(16).float()), TypeError),
+    (dict(dq_mode="bogus"), ValueError),
+])
+def test_binding_bwd_rejects_mismatched_tensors(over, exc):
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    with pytest.raises(exc):
+        attn.bwd(**_bwd_args(**over))
+
+
+@pytest.mark.parametrize("over,exc", [
+    (dict(out=_t(1, 2, 8, 64)), ValueError),
+    (dict(out=_t(1, 2, 8, 32).half()), TypeError),
+    (dict(lse=_t(1, 2, 8)), TypeError),
+    (dict(lse=_t(2, 1, 8).float()), ValueError),
+    (dict(k=_t(1, 2, 16, 64).half()), TypeError),
+    (dict(layout="sbhd"), ValueError),
+])
+def test_binding_fwd_rejects_mismatched_tensors(over, exc):
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    a = dict(q=_t(1, 2, 8, 64), k=_t(1, 2, 16, 64), v=_t(1, 2, 16, 32))
+    a.update(over)
+    with pytest.raises(exc):
+        attn.fwd(**a)
+
+
+def test_binding_bshd_shapes_checked():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    q, k, v = _t(1, 8, 2, 64), _t(1, 16, 2, 64), _t(1, 16, 2, 32)
+    with pytest.raises(ValueError):   # a [B, H, n, dv] o given to a [B, n, H, dim] call
+        attn.bwd(q, k, v, _t(1, 2, 8, 32), _t(1, 8, 2, 32), _t(1, 2, 8).float(), layout="bshd")
+    with pytest.raises(ValueError):   # shapes right, tensors on the CPU
+        attn.bwd(q, k, v, _t(1, 8, 2, 32), _t(1, 8, 2, 32), _t(1, 2, 8).float(), layout="bshd")
+
+
+def test_binding_proj_rejects_mismatched_outputs():
+    import torch
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    T, dm, hd = 16, 32, 32
+    with pytest.raises(TypeError):    # dW_O must be float32
+        attn.out_proj_bwd(_t(T, hd), _t(T, dm), _t(hd, dm), dw_o=_t(hd, dm))
+    with pytest.raises(TypeError):    # dO_cat in the input dtype
+        attn.out_proj_bwd(_t(T, hd), _t(T, dm), _t(hd, dm), do_cat=_t(T, hd).float())
+    with pytest.raises(ValueError):
+        attn.in_proj_bwd(_t(T, dm), _t(dm, hd), _t(dm, hd), _t(dm, hd), _t(T, hd), _t(T, hd),
+                         _t(T, hd), out={"dx": _t(T, dm + 8)})
+    with pytest.raises(TypeError):
+        attn.in_proj_bwd(_t(T, dm), _t(dm, hd), _t(dm, hd), _t(dm, hd), _t(T, hd), _t(T, hd),
+                         _t(T, hd), out={"dw_k": _t(dm, hd)})

@@ -97,6 +97,26 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous [B, H, seq, dim]")
 
 
+def _expect(t, name, shape, dtype):
+    """The library sizes every buffer from q's dtype and (B, H, n, m, d, dv):
+    a tensor of another shape or dtype would be read or written out of
+    bounds, so it is refused here, before anything reaches the C ABI."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(ref, *ts):
+    for t in ts:
+        if t.device != ref.device:
+            raise ValueError(f"all tensors must be on {ref.device}, got one on {t.device}")
+
+
+def _rows_shape(B, H, rows, width, layout):
+    return (B, rows, H, width) if layout == "bshd" else (B, H, rows, width)
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -106,6 +126,10 @@ def _shape(q, k, v, layout="bhsd"):
     ("bshd") tensors."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-d")
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}, got {layout!r}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"q, k, v must share a dtype, got {q.dtype}, {k.dtype}, {v.dtype}")
     if layout == "bshd":
         q, k, v = (t.transpose(1, 2) for t in (q, k, v))   # shape arithmetic only
     B, H, n, d = q.shape
@@ -144,26 +168,34 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, mask=None, seqlen
     tensors; LSE stays [B, H, n]).
     """
     lib = load()
-    _check_dev(q, k, v)
     B, H, n, m, d, dv = _shape(q, k, v, layout)
+    code = _dtype_code(q)
+    oshape = _rows_shape(B, H, n, dv, layout)
+    if out is not None:
+        _expect(out, "out", oshape, q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", (B, H, n), torch.float32)
+    _check_dev(q, k, v)
+    _same_device(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        oshape = (B, n, H, dv) if layout == "bshd" else (B, H, n, dv)
         out = torch.empty(oshape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
     _check_dev(out, lse)
+    _same_device(q, out, lse)
     if mask is None and seqlens_q is None and seqlens_k is None and layout == "bhsd":
         st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n, m, d, dv,
-                          float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+                          float(scale), int(bool(causal)), code, _stream(q))
         where = "attn_fwd"
     else:
-        code = _mask_code(causal, mask)
+        mcode = _mask_code(causal, mask)
         sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
+        _same_device(q, *(t for t in (sq, sk) if t is not None))
         st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sq), _ptr(sk),
-                             B, H, n, m, d, dv, float(scale), code, LAYOUTS[layout],
-                             _dtype_code(q), _stream(q))
+                             B, H, n, m, d, dv, float(scale), mcode, LAYOUTS[layout],
+                             code, _stream(q))
         where = "attn_fwd_ex"
     if st != ATTN_OK:
         raise AttnError(st, where)
@@ -187,15 +219,26 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     per-batch lengths and ``layout`` select attn_bwd_ex, as in fwd().
     """
     lib = load()
-    _check_dev(q, k, v, o, do, lse)
     B, H, n, m, d, dvw = _shape(q, k, v, layout)
+    code = _dtype_code(q)
+    _expect(o, "o", _rows_shape(B, H, n, dvw, layout), q.dtype)
+    _expect(do, "do", _rows_shape(B, H, n, dvw, layout), q.dtype)
+    _expect(lse, "lse", (B, H, n), torch.float32)
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        if t is not None:
+            _expect(t, name, ref.shape, q.dtype)
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError(f"workspace must be torch.uint8, got {workspace.dtype}")
+    if dq_mode not in DQ_MODES:
+        raise ValueError(f"dq_mode must be one of {sorted(DQ_MODES)}, got {dq_mode!r}")
+    _check_dev(q, k, v, o, do, lse)
+    _same_device(q, k, v, o, do, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     flags = DQ_MODES[dq_mode]
     if stages:
         for s_ in stages:
             flags |= STAGES[s_]
-    code = _dtype_code(q)
     need = int(lib.attn_bwd_workspace_bytes(B, H, n, m, d, dvw, code, flags))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -203,6 +246,7 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _check_dev(dq, dk, dv, workspace)
+    _same_device(q, dq, dk, dv, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     if mask is None and seqlens_q is None and seqlens_k is None and layout == "bhsd":
         st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
@@ -212,6 +256,7 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     else:
         mcode = _mask_code(causal, mask)
         sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
+        _same_device(q, *(t for t in (sq, sk) if t is not None))
         st = lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), _ptr(sq), _ptr(sk), B, H, n, m, d, dvw,
                              float(scale), mcode, LAYOUTS[layout], code, flags, _ptr(workspace),
@@ -222,10 +267,11 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     return dq, dk, dv
 
 
-def _mat(t, rows, cols, name):
+def _mat(t, rows, cols, name, dtype=None):
     if t.dim() != 2 or tuple(t.shape) != (rows, cols):
         raise ValueError(f"{name} must be [{rows}, {cols}], got {tuple(t.shape)}")
-    _check_dev(t)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
 def out_proj_bwd(o_cat, g, w_o, dw_o=None, do_cat=None):
@@ -243,8 +289,10 @@ def out_proj_bwd(o_cat, g, w_o, dw_o=None, do_cat=None):
         raise TypeError("o_cat, g and w_o must share a dtype")
     dw_o = torch.empty((hdv, dm), dtype=torch.float32, device=g.device) if dw_o is None else dw_o
     do_cat = torch.empty((T, hdv), dtype=g.dtype, device=g.device) if do_cat is None else do_cat
-    _mat(dw_o, hdv, dm, "dw_o")
-    _mat(do_cat, T, hdv, "do_cat")
+    _mat(dw_o, hdv, dm, "dw_o", torch.float32)
+    _mat(do_cat, T, hdv, "do_cat", g.dtype)
+    _check_dev(o_cat, g, w_o, dw_o, do_cat)
+    _same_device(g, o_cat, w_o, dw_o, do_cat)
     st = lib.attn_out_proj_bwd(_ptr(o_cat), _ptr(g), _ptr(w_o), _ptr(dw_o), _ptr(do_cat), T, dm,
                                hdv, _dtype_code(g), _stream(g))
     if st != ATTN_OK:
@@ -272,6 +320,12 @@ def in_proj_bwd(x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat, out=None):
     o.setdefault("dw_k", torch.empty((dm, hd), dtype=torch.float32, device=dev))
     o.setdefault("dw_v", torch.empty((dm, hdv), dtype=torch.float32, device=dev))
     o.setdefault("dx", torch.empty((T, dm), dtype=x.dtype, device=dev))
+    for name, r, c, dt in (("dw_q", dm, hd, torch.float32), ("dw_k", dm, hd, torch.float32),
+                           ("dw_v", dm, hdv, torch.float32), ("dx", T, dm, x.dtype)):
+        _mat(o[name], r, c, name, dt)
+    _check_dev(x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat,
+               *(o[n_] for n_ in ("dw_q", "dw_k", "dw_v", "dx")))
+    _same_device(x, w_q, w_k, w_v, dq_cat, dk_cat, dv_cat, *(o[n_] for n_ in ("dw_q", "dw_k", "dw_v", "dx")))
     st = lib.attn_in_proj_bwd(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(dq_cat),
                               _ptr(dk_cat), _ptr(dv_cat), _ptr(o["dw_q"]), _ptr(o["dw_k"]),
                               _ptr(o["dw_v"]), _ptr(o["dx"]), T, dm, hd, hdv, _dtype_code(x),
