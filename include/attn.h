@@ -89,17 +89,40 @@ enum attn_status {
     ATTN_EHIP = 5             /* the HIP runtime refused a launch */
 };
 
-/* attn_bwd flags.  Bits 0-3 choose how dQ is accumulated. */
+/*
+ * attn_bwd flags.  Bits 0-3 choose how dQ = scale * dS K (eulerpad P5) is
+ * accumulated; the keys of each row contribute from several workgroups of
+ * the dK/dV kernel, which owns a block of 256 keys and walks the queries.
+ *
+ *  ATTN_DQ_SEPARATE  a second pass per block of query rows recomputes P, dP
+ *                    and dS over the keys and sums dS K in registers:
+ *                    deterministic, no atomics, about 40% more matrix work.
+ *  ATTN_DQ_ATOMIC    the dK/dV kernel also forms dS K for its keys and adds
+ *                    it to a float32 accumulator in the workspace with
+ *                    atomic adds; a convert pass writes dq.  The key blocks
+ *                    before ATTN_DQ_SPLIT(k) (k blocks of 256 keys; 0 = none)
+ *                    are summed instead by the separate pass, which then
+ *                    initialises the accumulator.  Float32 addition is not
+ *                    associative, so dq can differ in its last bits from run
+ *                    to run; dk and dv are deterministic in every mode.
+ *                    16-bit dtypes only.
+ *  ATTN_DQ_AUTO      the library's choice of mode and split for the shapes,
+ *                    from measurements on MI355X.
+ */
+#define ATTN_DQ_SPLIT(k) ((int)(k) << 12) /* k in 0..255, with ATTN_DQ_ATOMIC only */
 enum attn_bwd_flags {
-    ATTN_DQ_AUTO = 0,         /* library's choice (currently ATTN_DQ_SEPARATE) */
-    ATTN_DQ_SEPARATE = 1,     /* a second pass per query tile recomputes P and dS:
-                                 deterministic, no atomics */
+    ATTN_DQ_AUTO = 0,
+    ATTN_DQ_ATOMIC = 1,
+    ATTN_DQ_SEPARATE = 2,
     /* Bits 8-10 restrict which kernels run (0 = all).  They exist so that
        each kernel can be timed on its own; a caller wanting gradients
        leaves them 0.  Later stages read what earlier ones wrote (the
        preprocess before the other two).  A 16-bit call that includes both
        the preprocess and dQ does the preprocess inside the dQ pass, which
-       then runs before dK/dV; the results are the same bits either way. */
+       then runs before dK/dV; the results are the same bits either way.
+       With ATTN_DQ_ATOMIC the dQ stage is the separate pass over the keys
+       before the split plus the convert pass, and only a call with every
+       stage yields dq. */
     ATTN_STAGE_PREPROCESS = 1 << 8,   /* D = rowsum(dO o O), LSE rescale */
     ATTN_STAGE_DKDV = 1 << 9,         /* dK and dV */
     ATTN_STAGE_DQ = 1 << 10           /* dQ */
@@ -136,8 +159,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int layout, int dtype, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes (a multiple of
- * 256; zero for an empty problem).  Holds per-row D and rescaled LSE.
+ * Bytes of device workspace attn_bwd needs for these sizes and flags (a
+ * multiple of 256; zero for an empty problem).  Holds per-row D and
+ * rescaled LSE, and with ATTN_DQ_ATOMIC or ATTN_DQ_AUTO (16-bit dtypes) the
+ * float32 dQ accumulator, B*H*round_up(n, 128)*(64 or 128) floats.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags);

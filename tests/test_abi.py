@@ -41,14 +41,29 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # two float32 arrays of B*H*round_up(n, 128) rows, rounded to 256 bytes
-    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128) == 2 * 64 * 4096 * 4
-    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64) == 2 * 128 * 4
+    # separate dQ pass: two float32 arrays of B*H*round_up(n, 128) rows
+    # (rounded to 256 bytes); the atomic and automatic modes add the float32
+    # dQ accumulator, rows x (64 or 128, the tile width for d)
+    sep, atom = B.ATTN_DQ_SEPARATE, B.ATTN_DQ_ATOMIC
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="separate") == \
+        2 * 64 * 4096 * 4
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128) == 64 * 4096 * 4 * (2 + 128)
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="atomic") == \
+        64 * 4096 * 4 * (2 + 128)
+    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64, dq_mode="separate") == 2 * 128 * 4
+    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64) == 128 * 4 * (2 + 64)
     assert attn.bwd_workspace_bytes(1, 1, 0, 5, 64, 64) == 0
     assert attn.bwd_workspace_bytes(0, 4, 100, 5, 64, 64) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 100, 100, B.ATTN_BF16, 0) == 0  # unsupported
     for code in (B.ATTN_BF16, B.ATTN_F16, B.ATTN_F32):
-        assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, 0) == 2 * 6 * 384 * 4
+        assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, sep) == 2 * 6 * 384 * 4
+    for code in (B.ATTN_BF16, B.ATTN_F16):
+        assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, atom) == \
+            6 * 384 * 4 * (2 + 64)
+        assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 96, 64, code, atom) == \
+            6 * 384 * 4 * (2 + 128)
+    # float32 has no fused dQ: no accumulator in any mode
+    assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, B.ATTN_F32, 0) == 2 * 6 * 384 * 4
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 64, 136, B.ATTN_F16, 0) == 0  # unsupported
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 96, 40, B.ATTN_F16, 0) > 0
 
@@ -115,6 +130,34 @@ def test_workspace_checks(lib):
 def test_unknown_flags(lib):
     assert _bwd(lib, flags=1 << 20) == B.ATTN_EUNSUPPORTED
     assert _bwd(lib, flags=7) == B.ATTN_EUNSUPPORTED
+    assert _bwd(lib, flags=3) == B.ATTN_EUNSUPPORTED
+    # a split only with the atomic mode; the atomic mode only for 16-bit types
+    assert _bwd(lib, flags=B.ATTN_DQ_SEPARATE | (1 << B.DQ_SPLIT_SHIFT)) == B.ATTN_EUNSUPPORTED
+    assert _bwd(lib, flags=B.ATTN_DQ_AUTO | (2 << B.DQ_SPLIT_SHIFT)) == B.ATTN_EUNSUPPORTED
+    assert _bwd(lib, flags=B.ATTN_DQ_ATOMIC, dtype=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
+
+
+def test_dq_flag_constants_match_header():
+    text = open(HEADER).read()
+    body = re.search(r"enum attn_bwd_flags \{(.*?)\};", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    vals = dict((k.strip(), v.strip()) for k, v in (e.split("=") for e in body.split(",") if "=" in e))
+    assert int(vals["ATTN_DQ_AUTO"]) == B.ATTN_DQ_AUTO == 0
+    assert int(vals["ATTN_DQ_ATOMIC"]) == B.ATTN_DQ_ATOMIC == 1
+    assert int(vals["ATTN_DQ_SEPARATE"]) == B.ATTN_DQ_SEPARATE == 2
+    m = re.search(r"#define ATTN_DQ_SPLIT\(k\) \(\(int\)\(k\) << (\d+)\)", text)
+    assert m and int(m.group(1)) == B.DQ_SPLIT_SHIFT
+
+
+def test_binding_dq_split_arguments():
+    assert B._dq_flags("atomic", 3) == B.ATTN_DQ_ATOMIC | (3 << B.DQ_SPLIT_SHIFT)
+    assert B._dq_flags("separate", None) == B.ATTN_DQ_SEPARATE
+    with pytest.raises(ValueError):
+        B._dq_flags("separate", 1)
+    with pytest.raises(ValueError):
+        B._dq_flags("atomic", 256)
+    with pytest.raises(ValueError):
+        B._dq_flags("fused", None)
 
 
 def test_empty_problems_need_no_pointers(lib):

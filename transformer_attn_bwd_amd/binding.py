@@ -20,14 +20,15 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
-ATTN_DQ_AUTO, ATTN_DQ_SEPARATE = 0, 1
+ATTN_DQ_AUTO, ATTN_DQ_ATOMIC, ATTN_DQ_SEPARATE = 0, 1, 2
+DQ_SPLIT_SHIFT, DQ_SPLIT_MAX = 12, 255
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
          "causal_bottom_right": ATTN_MASK_CAUSAL_BOTTOM_RIGHT}
 ATTN_LAYOUT_BHSD, ATTN_LAYOUT_BSHD = 0, 1
 LAYOUTS = {"bhsd": ATTN_LAYOUT_BHSD, "bshd": ATTN_LAYOUT_BSHD}
 ATTN_STAGE_PREPROCESS, ATTN_STAGE_DKDV, ATTN_STAGE_DQ = 1 << 8, 1 << 9, 1 << 10
-DQ_MODES = {"auto": ATTN_DQ_AUTO, "separate": ATTN_DQ_SEPARATE}
+DQ_MODES = {"auto": ATTN_DQ_AUTO, "atomic": ATTN_DQ_ATOMIC, "separate": ATTN_DQ_SEPARATE}
 STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
@@ -202,21 +203,37 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, mask=None, seqlen
     return out, lse
 
 
+def _dq_flags(dq_mode, dq_split):
+    if dq_mode not in DQ_MODES:
+        raise ValueError(f"dq_mode must be one of {sorted(DQ_MODES)}, got {dq_mode!r}")
+    flags = DQ_MODES[dq_mode]
+    if dq_split is not None:
+        if dq_mode != "atomic":
+            raise ValueError("dq_split applies to dq_mode='atomic' only")
+        if not 0 <= int(dq_split) <= DQ_SPLIT_MAX:
+            raise ValueError(f"dq_split must be in 0..{DQ_SPLIT_MAX}")
+        flags |= int(dq_split) << DQ_SPLIT_SHIFT
+    return flags
+
+
 def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto"):
     code = _DTYPE_CODES.get(dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {dtype}; use bfloat16, float16 or float32")
-    return int(load().attn_bwd_workspace_bytes(B, H, n, m, d, dv, code, DQ_MODES[dq_mode]))
+    return int(load().attn_bwd_workspace_bytes(B, H, n, m, d, dv, code, _dq_flags(dq_mode, None)))
 
 
 def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace=None,
         dq=None, dk=None, dv=None, stages=None, mask=None, seqlens_q=None, seqlens_k=None,
-        layout="bhsd"):
+        layout="bhsd", dq_split=None):
     """(dq, dk, dv) with the shapes and dtype of (q, k, v).
 
-    ``stages`` (a subset of {"preprocess", "dkdv", "dq"}) restricts which
-    kernels run; it exists for timing single kernels.  ``mask`` and the
-    per-batch lengths and ``layout`` select attn_bwd_ex, as in fwd().
+    ``dq_mode`` is "auto", "separate" or "atomic" (ATTN_DQ_*), and
+    ``dq_split`` the number of leading 256-key blocks whose dQ the separate
+    pass sums in the atomic mode.  ``stages`` (a subset of {"preprocess",
+    "dkdv", "dq"}) restricts which kernels run; it exists for timing single
+    kernels.  ``mask`` and the per-batch lengths and ``layout`` select
+    attn_bwd_ex, as in fwd().
     """
     lib = load()
     B, H, n, m, d, dvw = _shape(q, k, v, layout)
@@ -229,13 +246,11 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
             _expect(t, name, ref.shape, q.dtype)
     if workspace is not None and workspace.dtype != torch.uint8:
         raise TypeError(f"workspace must be torch.uint8, got {workspace.dtype}")
-    if dq_mode not in DQ_MODES:
-        raise ValueError(f"dq_mode must be one of {sorted(DQ_MODES)}, got {dq_mode!r}")
+    flags = _dq_flags(dq_mode, dq_split)
     _check_dev(q, k, v, o, do, lse)
     _same_device(q, k, v, o, do, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    flags = DQ_MODES[dq_mode]
     if stages:
         for s_ in stages:
             flags |= STAGES[s_]

@@ -14,6 +14,9 @@ using attn::Workspace;
 constexpr int kMaxSeq = 1 << 22;          // n, m limit (grid y dimension and int math)
 constexpr int kStageMask = ATTN_STAGE_PREPROCESS | ATTN_STAGE_DKDV | ATTN_STAGE_DQ;
 constexpr int kDqModeMask = 0xF;
+constexpr int kSplitShift = 12;
+constexpr int kSplitMask = 0xFF << kSplitShift;
+static_assert(ATTN_DQ_SPLIT(1) == 1 << kSplitShift, "split field of the C ABI");
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -83,15 +86,83 @@ bool tensor_ok(const void* p, long elems, int dtype) {
     return aligned(p, is_16bit(dtype) ? 16 : 4);
 }
 
-size_t workspace_bytes(const Problem& p) {
+// Width of the float32 dQ accumulator's rows: the 16-bit kernels' tile
+// width for d.
+int acc_width(const Problem& p) { return (attn::mfma_widths(p) >> 8) == 0x40 ? 64 : 128; }
+
+// Whether the flags' dQ mode can need the accumulator (ATTN_DQ_AUTO may pick
+// the atomic mode, so it reserves the space too).
+bool may_use_acc(const Problem& p, int flags) {
+    const int mode = flags & kDqModeMask;
+    return is_16bit(p.dtype) && (mode == ATTN_DQ_ATOMIC || mode == ATTN_DQ_AUTO);
+}
+
+size_t workspace_bytes(const Problem& p, int flags) {
     if (p.heads() == 0 || p.n == 0) return 0;
     const size_t rows = (size_t)p.heads() * (size_t)attn::padded_rows(p.n);
-    return round_up(2 * rows * sizeof(float), 256);
+    size_t bytes = round_up(2 * rows * sizeof(float), 256);
+    if (may_use_acc(p, flags)) bytes += round_up(rows * acc_width(p) * sizeof(float), 256);
+    return bytes;
+}
+
+// How dQ is accumulated for a 16-bit backward: -1 for the separate pass,
+// else the number of leading 256-key blocks the separate pass sums before
+// the fused dK/dV kernel adds the rest with atomics.
+int resolve_dq(const Problem& p, int flags) {
+    const int mode = flags & kDqModeMask;
+    if (!is_16bit(p.dtype) || mode == ATTN_DQ_SEPARATE) return -1;
+    if (mode == ATTN_DQ_ATOMIC) return (flags & kSplitMask) >> kSplitShift;
+    return -1;   // ATTN_DQ_AUTO
 }
 
 int hip_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+constexpr int kNoKeyLimit = 0x7fffffff;
+
+// The 16-bit backward with the fused dQ: the separate pass over the keys of
+// the first `split` 256-key blocks (with the preprocess in its prologue)
+// initialises the float32 accumulator, the dK/dV kernel adds dS K for the
+// later key blocks with atomics, and the convert pass writes dq.
+template <typename T>
+int bwd_atomic_t(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv_out,
+                 const attn::Workspace& w, int split, int stages, hipStream_t s) {
+    const long lim = (long)split * attn::kDkdvBlock;
+    const int key_limit = lim > kNoKeyLimit ? kNoKeyLimit : (int)lim;
+    const bool pre = (stages & ATTN_STAGE_PREPROCESS) != 0, dqs = (stages & ATTN_STAGE_DQ) != 0;
+    int st;
+    if (p.n > 0 && dqs) {
+        if (!attn::launch_bwd_dq_mfma<T>(p, q, k, v, dout, pre ? o : nullptr, pre ? lse : nullptr,
+                                         w, nullptr, w.dqacc, key_limit, s))
+            return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    } else if (p.n > 0 && pre) {
+        if (!attn::launch_bwd_preprocess_mfma<T>(p, o, dout, lse, w, s)) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (stages & ATTN_STAGE_DKDV) {
+        if (!attn::launch_bwd_dkdv_dqa_mfma<T>(p, q, k, v, dout, w, dk, dv_out, w.dqacc, key_limit,
+                                               s))
+            return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (p.n > 0 && dqs) {
+        attn::launch_dq_convert<T>(p, w, dq, s);
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    return ATTN_OK;
+}
+
+int bwd_atomic(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv_out,
+               const attn::Workspace& w, int split, int stages, hipStream_t s) {
+    return p.dtype == ATTN_BF16
+               ? bwd_atomic_t<__bf16>(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, split, stages, s)
+               : bwd_atomic_t<_Float16>(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, split, stages,
+                                        s);
 }
 
 // Sizes of the projection calls: T >= 0, widths multiples of 8 (16-byte
@@ -176,10 +247,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags) {
-    (void)flags;
     Problem p;
     if (check_problem(B, H, n, m, d, dv, 1.f, 0, dtype, &p) != ATTN_OK) return 0;
-    return workspace_bytes(p);
+    return workspace_bytes(p, flags);
 }
 
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -194,9 +264,12 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     if (!lens_ok(seqlens_q) || !lens_ok(seqlens_k)) return ATTN_EINVAL;
     p.seqlens_q = seqlens_q;
     p.seqlens_k = seqlens_k;
-    if (flags & ~(kDqModeMask | kStageMask)) return ATTN_EUNSUPPORTED;
+    if (flags & ~(kDqModeMask | kStageMask | kSplitMask)) return ATTN_EUNSUPPORTED;
     const int dq_mode = flags & kDqModeMask;
-    if (dq_mode != ATTN_DQ_AUTO && dq_mode != ATTN_DQ_SEPARATE) return ATTN_EUNSUPPORTED;
+    if (dq_mode != ATTN_DQ_AUTO && dq_mode != ATTN_DQ_SEPARATE && dq_mode != ATTN_DQ_ATOMIC)
+        return ATTN_EUNSUPPORTED;
+    if ((flags & kSplitMask) && dq_mode != ATTN_DQ_ATOMIC) return ATTN_EUNSUPPORTED;
+    if (dq_mode == ATTN_DQ_ATOMIC && !is_16bit(dtype)) return ATTN_EUNSUPPORTED;
     const long hq = p.heads() * (long)n, hk = p.heads() * (long)m;
     if (!tensor_ok(q, hq * d, dtype) || !tensor_ok(k, hk * d, dtype) ||
         !tensor_ok(v, hk * dv, dtype) || !tensor_ok(o, hq * dv, dtype) ||
@@ -204,7 +277,7 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
         !tensor_ok(dq, hq * d, dtype) || !tensor_ok(dk, hk * d, dtype) ||
         !tensor_ok(dv_out, hk * dv, dtype))
         return ATTN_EINVAL;
-    const size_t need = workspace_bytes(p);
+    const size_t need = workspace_bytes(p, flags);
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes_given < need) return ATTN_EWORKSPACE;
         if (!aligned(workspace, 16)) return ATTN_EINVAL;
@@ -221,6 +294,12 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     (void)hipGetLastError();
 
     const bool bf = is_16bit(dtype);
+    const int split = resolve_dq(p, flags);
+    if (split >= 0) {
+        w.dqacc = (float*)((char*)workspace + round_up(2 * (size_t)p.heads() * w.n_pad * 4, 256));
+        w.acc_w = acc_width(p);
+        return bwd_atomic(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, split, stages, s);
+    }
     // 16-bit calls that run both the preprocess and the dQ pass fold the
     // former into the latter's prologue (same bits), which then runs before
     // the dK/dV kernel that reads its results.
@@ -229,8 +308,10 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     bool ok = true;
     if (fused) {
         ok = dtype == ATTN_BF16
-                 ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, o, lse, w, dq, s)
-                 : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, o, lse, w, dq, s);
+                 ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, o, lse, w, dq, nullptr,
+                                                    kNoKeyLimit, s)
+                 : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, o, lse, w, dq, nullptr,
+                                                      kNoKeyLimit, s);
         if (!ok) return ATTN_EUNSUPPORTED;
         if ((st = hip_status()) != ATTN_OK) return st;
     }
@@ -255,9 +336,9 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     if (n > 0 && (stages & ATTN_STAGE_DQ) && !fused) {
         ok = bf ? (dtype == ATTN_BF16
                        ? attn::launch_bwd_dq_mfma<__bf16>(p, q, k, v, dout, nullptr, nullptr,
-                                                          w, dq, s)
+                                                          w, dq, nullptr, kNoKeyLimit, s)
                        : attn::launch_bwd_dq_mfma<_Float16>(p, q, k, v, dout, nullptr, nullptr,
-                                                            w, dq, s))
+                                                            w, dq, nullptr, kNoKeyLimit, s))
                 : attn::launch_bwd_dq_f32(p, (const float*)q, (const float*)k, (const float*)v,
                                           (const float*)dout, w, (float*)dq, s);
         if (!ok) return ATTN_EUNSUPPORTED;

@@ -39,12 +39,18 @@ struct DqCfg {
     static constexpr int PD = 4;              // operand reads issued ahead
 };
 
+// With dqacc non-null the pass covers only the keys before key_limit (the
+// rest reach dQ through the atomics of the fused dK/dV kernel) and writes
+// its unscaled float32 sums to dqacc, [B*H][n_pad][D], every row of its
+// tile below n_pad (padded rows as zeros); otherwise it covers every key
+// and writes dQ = scale * sum in T.
 template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, float* __restrict__ lse2, float* __restrict__ Dw,
-    const T* __restrict__ o, const float* __restrict__ lse, T* __restrict__ dq, int n, int m,
-    int dg, int dvg, int n_pad, float scale, float c2, SeqInfo si) {
+    const T* __restrict__ o, const float* __restrict__ lse, T* __restrict__ dq,
+    float* __restrict__ dqacc, int key_limit, int n, int m, int dg, int dvg, int n_pad,
+    float scale, float c2, SeqInfo si) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
     // One LDS variable per buffer: the compiler can then tell that reads
@@ -67,8 +73,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
-    const long bh = blockIdx.x;
-    const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+    const TileOrder to = tile_order((int)gridDim.x, (int)gridDim.y);
+    const long bh = to.head;
+    const int qb = CAUSAL ? (int)gridDim.y - 1 - to.rank : to.rank;
     const int i0 = qb * C::BM;
     // This head's query and key lengths and causal offset: rows i < nb take
     // part, keys j < mb, and key j is visible from row i when j <= i + off.
@@ -164,6 +171,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     int k_end = CAUSAL ? min(mb, i0 + C::BM + off) : mb;
     if (i0 >= nb) k_end = 0;
+    k_end = min(k_end, key_limit);
     const int nsteps = (max(k_end, 0) + BN - 1) / BN;
     // Leading steps that need no mask: keys visible from the workgroup's
     // first query (causal) and inside the mb keys.  The rest are masked.
@@ -334,9 +342,40 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // Accumulator slot vv of tile (x, t) holds column d = 32x + 8(vv>>2) +
     // 4g + (vv&3) of query myq[t].  The tiles go out through this wave's
-    // staging rows in LDS, 64 columns at a time: written row-major (16-byte
-    // chunks XOR-swizzled by row), read back as whole rows and stored 16
-    // bytes per lane, eight 128-byte row segments per instruction.
+    // staging rows in LDS: written row-major (16-byte chunks XOR-swizzled by
+    // row), read back as whole rows and stored 16 bytes per lane, eight
+    // 128-byte row segments per instruction.
+    if (dqacc != nullptr) {
+        // float32 partial sums, 32 columns (128 bytes) per staged row; the
+        // chunk swizzle by (row >> 1) & 7 keeps both the 16-byte writes (16
+        // rows per lane group) and the row reads free of bank conflicts
+        float* regf = reinterpret_cast<float*>(sE) + wave * 64 * 32;
+        float* acc_head = dqacc + bh * (long)n_pad * D;
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = 32 * t + li;
+#pragma unroll
+                for (int vq = 0; vq < 4; ++vq) {
+                    const int chunk = 2 * vq + g;
+                    *reinterpret_cast<f32x4*>(regf + row * 32 + 4 * (chunk ^ ((row >> 1) & 7))) =
+                        f32x4{acc[x][t][4 * vq], acc[x][t][4 * vq + 1], acc[x][t][4 * vq + 2],
+                              acc[x][t][4 * vq + 3]};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int lin = 64 * i + lane, row = lin >> 3, chunk = lin & 7;
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(
+                    regf + row * 32 + 4 * (chunk ^ ((row >> 1) & 7)));
+                const int query = i0 + (C::BM / 2) * (row / 32) + 32 * wave + row % 32;
+                if (query < n_pad)
+                    *reinterpret_cast<f32x4*>(acc_head + (long)query * D + 32 * x + 4 * chunk) = w4;
+            }
+        }
+        return;
+    }
     T* reg = sE + wave * 64 * 64;
 #pragma unroll
     for (int sl = 0; sl < D / 64; ++sl) {
@@ -371,7 +410,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
 template <typename T, int D, int DV>
 void launch_dq(const Problem& p, const void* q, const void* k, const void* v, const void* dout,
-               const void* o, const float* lse, const Workspace& w, void* dq, hipStream_t s) {
+               const void* o, const float* lse, const Workspace& w, void* dq, float* dqacc,
+               int key_limit, hipStream_t s) {
     using C = DqCfg<D, DV>;
     dim3 grid((unsigned)p.heads(), (unsigned)((p.n + C::BM - 1) / C::BM));
     const float c2 = p.scale * kLog2e;
@@ -379,11 +419,35 @@ void launch_dq(const Problem& p, const void* q, const void* k, const void* v, co
     if (p.causal)
         bwd_dq_kernel<T, D, DV, true><<<grid, 64 * C::NW, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D, (const T*)o,
-            lse, (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+            lse, (T*)dq, dqacc, key_limit, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
     else
         bwd_dq_kernel<T, D, DV, false><<<grid, 64 * C::NW, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D, (const T*)o,
-            lse, (T*)dq, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+            lse, (T*)dq, dqacc, key_limit, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+}
+
+// dQ = scale * dqacc in T, for the rows i < n of every head (the
+// accumulator's padded rows and columns are not copied); one thread per
+// eight columns.
+template <typename T>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ dqacc,
+                                                         T* __restrict__ dq, int n, int n_pad,
+                                                         int acc_w, int dg, float scale,
+                                                         long total, SeqInfo si) {
+    const long id = (long)blockIdx.x * 256 + threadIdx.x;
+    if (id >= total) return;
+    const int cpr = dg / 8;
+    const long rowid = id / cpr;
+    const int c8 = (int)(id - rowid * cpr);
+    const long bh = rowid / n;
+    const int i = (int)(rowid - bh * n);
+    const float* src = dqacc + (bh * (long)n_pad + i) * acc_w + 8 * c8;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+    const HeadView hv = head_view(si, bh, n, dg);
+    *reinterpret_cast<vec8<T>*>(dq + hv.base + (long)i * hv.stride + 8 * c8) =
+        pack8<T>(a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale, b[0] * scale,
+                 b[1] * scale, b[2] * scale, b[3] * scale);
 }
 
 }  // namespace
@@ -391,15 +455,24 @@ void launch_dq(const Problem& p, const void* q, const void* k, const void* v, co
 template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const void* o, const float* lse, const Workspace& w,
-                        void* dq, hipStream_t s) {
+                        void* dq, float* dqacc, int key_limit, hipStream_t s) {
     switch (mfma_widths(p)) {
-    case 0x4040: launch_dq<T, 64, 64>(p, q, k, v, dout, o, lse, w, dq, s); break;
-    case 0x4080: launch_dq<T, 64, 128>(p, q, k, v, dout, o, lse, w, dq, s); break;
-    case 0x8040: launch_dq<T, 128, 64>(p, q, k, v, dout, o, lse, w, dq, s); break;
-    case 0x8080: launch_dq<T, 128, 128>(p, q, k, v, dout, o, lse, w, dq, s); break;
+    case 0x4040: launch_dq<T, 64, 64>(p, q, k, v, dout, o, lse, w, dq, dqacc, key_limit, s); break;
+    case 0x4080: launch_dq<T, 64, 128>(p, q, k, v, dout, o, lse, w, dq, dqacc, key_limit, s); break;
+    case 0x8040: launch_dq<T, 128, 64>(p, q, k, v, dout, o, lse, w, dq, dqacc, key_limit, s); break;
+    case 0x8080: launch_dq<T, 128, 128>(p, q, k, v, dout, o, lse, w, dq, dqacc, key_limit, s); break;
     default: return false;
     }
     return true;
+}
+
+template <typename T>
+void launch_dq_convert(const Problem& p, const Workspace& w, void* dq, hipStream_t s) {
+    const long total = p.heads() * (long)p.n * (p.d / 8);
+    if (total == 0) return;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    dq_convert_kernel<T><<<blocks, 256, 0, s>>>(w.dqacc, (T*)dq, p.n, w.n_pad, w.acc_w, p.d,
+                                                p.scale, total, seq_info(p));
 }
 
 // Each element type is compiled as its own object (-DATTN_ELEM=bf16 or f16)
@@ -409,6 +482,7 @@ bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const vo
 #endif
 template bool launch_bwd_dq_mfma<ATTN_ELEM>(const Problem&, const void*, const void*,
                                            const void*, const void*, const void*, const float*,
-                                           const Workspace&, void*, hipStream_t);
+                                           const Workspace&, void*, float*, int, hipStream_t);
+template void launch_dq_convert<ATTN_ELEM>(const Problem&, const Workspace&, void*, hipStream_t);
 
 }  // namespace attn

@@ -59,8 +59,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, li = lane & 31;
-    const long bh = blockIdx.x;
-    const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+    const TileOrder to = tile_order((int)gridDim.x, (int)gridDim.y);
+    const long bh = to.head;
+    const int qb = CAUSAL ? (int)gridDim.y - 1 - to.rank : to.rank;
     const int i0 = qb * C::BM;
     // This head's query and key lengths and causal offset: rows i < nb take
     // part, keys j < mb, and key j is visible from row i when j <= i + off.

@@ -52,6 +52,21 @@ inline SeqInfo seq_info(const Problem& p) {
             p.bshd ? 1 : 0};
 }
 
+// Workgroup order of the attention kernels, whose grids are (heads, blocks)
+// with blocks per head ranked so that rank 0 is the longest under a causal
+// mask.  The hardware hands the workgroups of a launch to the chip's eight
+// XCDs in turn, in linear order (x fastest): rank-major order starts the
+// longest blocks of every head first, and with B*H a multiple of 8 all
+// blocks of a head run on one XCD.
+struct TileOrder {
+    int head, rank;
+};
+__device__ __forceinline__ TileOrder tile_order(int heads, int nblk) {
+    (void)nblk;
+    const int b = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+    return {b % heads, b / heads};
+}
+
 // Where head bh's rows live in a tensor with `rows` rows of `width`
 // elements per head: element offset of its row 0, and the distance between
 // consecutive rows.  [B, H, seq, dim]: the head is one contiguous block;
@@ -85,11 +100,15 @@ __device__ __forceinline__ SeqLens seq_lens(const SeqInfo& si, long bh, int n, i
 constexpr int kRowPad = 128;
 inline int padded_rows(int n) { return (n + kRowPad - 1) / kRowPad * kRowPad; }
 
-// Workspace view: lse2 [B*H][n_pad] then D [B*H][n_pad], float32.
+// Workspace view: lse2 [B*H][n_pad] then D [B*H][n_pad], float32; with the
+// fused dQ also the float32 dQ accumulator dqacc [B*H][n_pad][acc_w], acc_w
+// the 16-bit kernels' tile width for d (64 or 128).
 struct Workspace {
     float* lse2;
     float* D;
     int n_pad;
+    float* dqacc = nullptr;
+    int acc_w = 0;
 };
 
 // 16-bit MFMA path, T = __bf16 or _Float16 (instantiated in the kernel
@@ -106,11 +125,24 @@ bool launch_bwd_dkdv_mfma(const Problem& p, const void* q, const void* k, const 
                           hipStream_t s);
 // With o and lse non-null the dQ pass also does the preprocess for its rows
 // (same bits as launch_bwd_preprocess_mfma) and writes it to w; with them
-// null it reads w.
+// null it reads w.  With dqacc non-null it covers only keys j < key_limit
+// and writes its unscaled float32 sums to dqacc (w.dqacc's layout) instead
+// of dq.
 template <typename T>
 bool launch_bwd_dq_mfma(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const void* o, const float* lse, const Workspace& w,
-                        void* dq, hipStream_t s);
+                        void* dq, float* dqacc, int key_limit, hipStream_t s);
+// The dK/dV kernel whose workgroups with first key >= dqa_from also add
+// their dS K to w.dqacc with atomics.
+template <typename T>
+bool launch_bwd_dkdv_dqa_mfma(const Problem& p, const void* q, const void* k, const void* v,
+                              const void* dout, const Workspace& w, void* dk, void* dv,
+                              float* dqacc, int dqa_from, hipStream_t s);
+// dq = scale * w.dqacc in T.
+template <typename T>
+void launch_dq_convert(const Problem& p, const Workspace& w, void* dq, hipStream_t s);
+// Keys per workgroup of the dK/dV kernel: the granularity of dqa_from.
+constexpr int kDkdvBlock = 256;
 
 // Projection gradients around attention (tokens as rows, T = B n):
 // matrices X [T, d_model], W_Q, W_K [d_model, hd], W_V [d_model, hdv],
