@@ -37,7 +37,8 @@ PEAK_HBM_GBS = 8000.0
 # same counters read for a plain 1 GiB device copy (x2.0 and x1.0).  They
 # hold only for the kernel sources they were taken on, identified by hash;
 # after any change to those sources the traffic is reported as null.
-KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dq_mfma.hip", "attn_device.h", "attn_launch.h")
+KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip", "attn_device.h",
+                  "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
     "sources_sha256": "7c90c0964c97c6b56e87ff4d5dbbd003c3ec7c4e1d43dd39522444875db6bdac",
@@ -81,6 +82,45 @@ def dq_flops(w) -> float:
     # S, dP recomputed, dQ += dS K
     f = 2.0 * w.n * w.m * (2 * w.d + w.dv) * w.B * w.H
     return f / 2 if w.causal else f
+
+
+def dkdv_bytes(w) -> float:
+    """Algorithmic HBM bytes of the dK/dV kernel: read Q, K, V, dO (16-bit),
+    LSE2 and D (float32); write dK and dV (16-bit)."""
+    e = 2
+    heads = w.B * w.H
+    reads = heads * (w.n * w.d + w.m * w.d + w.m * w.dv + w.n * w.dv) * e + heads * w.n * 8
+    writes = heads * (w.m * w.d + w.m * w.dv) * e
+    return float(reads + writes)
+
+
+def dq_bytes(w) -> float:
+    """Algorithmic HBM bytes of the dQ pass with its preprocess prologue:
+    read Q, K, V, O, dO (16-bit) and LSE (float32); write dQ (16-bit) and
+    LSE2 and D (float32)."""
+    e = 2
+    heads = w.B * w.H
+    reads = heads * (w.n * w.d + w.m * w.d + w.m * w.dv + 2 * w.n * w.dv) * e + heads * w.n * 4
+    writes = heads * w.n * w.d * e + heads * w.n * 8
+    return float(reads + writes)
+
+
+def roofline_bound(flops: float, nbytes: float) -> str:
+    """"mfma" when the kernel's arithmetic intensity (flop per algorithmic
+    HBM byte) is above the machine balance of dense bf16 MFMA over HBM
+    (2516.6 TFLOP/s / 8 TB/s = 315 flop/B), else "hbm"."""
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return "mfma" if flops / nbytes > ridge else "hbm"
+
+
+def pairs_from(w, key0: int) -> float:
+    """Visible (query, key) pairs with key index >= key0, over all heads."""
+    key0 = min(max(key0, 0), w.m)
+    if w.causal:
+        cnt = sum(max(0, w.n - j) for j in range(key0, w.m))
+    else:
+        cnt = w.n * (w.m - key0)
+    return float(cnt) * w.B * w.H
 
 
 def bwd_bytes(w) -> float:
@@ -166,12 +206,89 @@ def proj_bench(w, steps, torch, attn):
     }
 
 
+# the other workloads timed beside the headline, in both dQ modes
+TABLE_WORKLOADS = ("causal_1k_d64", "causal_4k_d128", "causal_16k_d128",
+                   "cross_512x2048_d128_dv64", "causal_4k_d128_fp16")
+
+
+def mode_figures(w, run, steps, torch, split=None):
+    """Whole-backward and per-kernel timings of one dQ mode."""
+    ms = time_loop(run, steps, torch, 2)
+    med = step_times(run, steps, torch)[steps // 2]
+    k_dkdv = time_loop(lambda: run(["dkdv"]), steps, torch, 2)
+    k_dq = time_loop(lambda: run(["preprocess", "dq"]), steps, torch, 2)
+    nkeys = (split or 0) * 256
+    if split is None:
+        f_dkdv, f_dq = dkdv_flops(w), dq_flops(w)
+    else:
+        # the fused kernel also forms dS K for the keys past the split; the
+        # separate pass recomputes S and dP only for the keys before it
+        frac_sep = 1.0 - pairs_from(w, nkeys) / pairs_from(w, 0)
+        f_dkdv = dkdv_flops(w) + 2.0 * w.d * pairs_from(w, nkeys)
+        f_dq = dq_flops(w) * frac_sep
+    kern = {"dkdv": (k_dkdv, f_dkdv), "dq": (k_dq, f_dq)}
+    dom = max(kern, key=lambda k_: kern[k_][0])
+    tf = bwd_flops(w) / (ms * 1e-3) / 1e12
+    out = {
+        "ms_mean": round(ms, 4), "ms_median": round(med, 4), "tflops": round(tf, 2),
+        "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"dkdv": round(k_dkdv, 4), "dq_with_preprocess": round(k_dq, 4)},
+        "dominant": dom,
+        "dominant_share_of_step": round(kern[dom][0] / ms, 3),
+        "dominant_frac_of_peak": round(kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
+                                       / PEAK_BF16_TFLOPS, 4),
+    }
+    if split is not None:
+        out["split"] = split
+    return out
+
+
+def workload_table(names, steps, torch, attn, make_inputs, workloads):
+    """For each workload: the backward in the separate-pass dQ mode and in
+    the atomic mode at the best of a few splits (leading 256-key blocks left
+    to the separate pass)."""
+    table = {}
+    dev = "cuda:0"
+    for name in names:
+        w = workloads[name]
+        print(f"bench: table {name} ...", file=sys.stderr, flush=True)
+        q, k, v, do = (t.to(dev) for t in make_inputs(w, "cpu"))
+        o, lse = attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        wss = {}
+
+        def runner(mode, split):
+            key = mode
+            if key not in wss:
+                wss[key] = torch.empty(max(attn.bwd_workspace_bytes(
+                    w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype, dq_mode=mode), 1),
+                    dtype=torch.uint8, device=dev)
+            return lambda stages=None: attn.bwd(
+                q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, dq_mode=mode,
+                dq_split=split, workspace=wss[key], dq=dq, dk=dk, dv=dv, stages=stages)
+
+        row = {"flops": bwd_flops(w),
+               "separate": mode_figures(w, runner("separate", None), steps, torch)}
+        nkb = (w.m + 255) // 256
+        splits = sorted({0} | {max(1, (nkb * f) // 8) for f in (1, 2, 3, 4, 6)})
+        tried = {sp: time_loop(runner("atomic", sp), max(3, steps // 2), torch, 2)
+                 for sp in splits}
+        best = min(tried, key=tried.get)
+        row["atomic"] = mode_figures(w, runner("atomic", best), steps, torch, best)
+        row["atomic"]["splits_ms"] = {str(sp): round(t, 4) for sp, t in tried.items()}
+        table[name] = row
+        del q, k, v, do, o, lse, dq, dk, dv, wss
+        torch.cuda.empty_cache()
+    return table
+
+
 def cpu_baseline(w, inputs, heads_wanted):
     """The float64 oracle's backward on a bounded sample of the workload's
     heads, on the host cores; reported in the metric's unit."""
     import numpy as np
     import oracle
     threads = oracle.num_threads()
+    affinity = len(os.sched_getaffinity(0))
     # about 20 s of float64 work at the headline size: four heads per thread
     nh = max(1, min(heads_wanted or 4 * threads, w.B * w.H))
     q, k, v, do = (t.reshape(w.B * w.H, *t.shape[2:])[:nh].double().numpy() for t in inputs)
@@ -185,7 +302,7 @@ def cpu_baseline(w, inputs, heads_wanted):
         "kind": "oracle",
         "sample": f"{nh} of {w.B * w.H} heads of {w.name} (float64 backward incl. recomputing "
                   f"P, O, D), {dt:.1f} s wall on {threads} OpenMP threads",
-        "seconds": dt, "heads": nh,
+        "seconds": dt, "heads": nh, "omp_threads": threads, "affinity_cpus": affinity,
     }
 
 
@@ -198,6 +315,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0)
     ap.add_argument("--no-proj", action="store_true", help="skip the projection-gradient timing")
+    ap.add_argument("--no-table", action="store_true",
+                    help="skip the other workloads and the atomic dQ mode")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (a known-traffic "
                          "reference for hardware byte counters)")
@@ -276,10 +395,14 @@ def main():
     dk_tf = dkdv_flops(w) / (kern_ms["dkdv"] * 1e-3) / 1e12
     dominant = max(("dkdv", "dq"), key=lambda kname: kern_ms[kname])
     dom_flops = dkdv_flops(w) if dominant == "dkdv" else dq_flops(w)
+    dom_bytes = dkdv_bytes(w) if dominant == "dkdv" else dq_bytes(w)
     dom_tf = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
+    mask = "causal" if w.causal else "non-causal"
+    shape = f"N={w.n}" if w.n == w.m else f"n={w.n}, m={w.m}"
+    dims = f"d={w.d}" if w.d == w.dv else f"d={w.d}, dv={w.dv}"
 
     result = {
-        "metric": "attn backward TFLOP/s (bf16, causal, d=128, N=4096) + % of MFMA peak",
+        "metric": f"attn backward TFLOP/s ({w.dtype}, {mask}, {dims}, {shape}) + % of MFMA peak",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -305,18 +428,23 @@ def main():
                                      / PEAK_BF16_TFLOPS, 2)},
         "roofline": {
             "kernel": f"bwd_{dominant}",
-            "bound": "mfma",
+            "bound": roofline_bound(dom_flops, dom_bytes),
             "achieved": round(dom_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(w.name, f"bwd_{dominant}"),
+            "algorithmic_bytes": dom_bytes,
         },
         "dkdv_tflops": round(dk_tf, 2),
         "hbm_algorithmic_GBps": round(bwd_bytes(w) / (ms * 1e-3) / 1e9, 1),
         "outputs_finite": ok,
         "wall_s_timed": round(t_wall, 3),
     }
+    if not args.no_table:
+        result["workloads"] = workload_table(
+            [x for x in TABLE_WORKLOADS], max(5, args.steps // 2), torch, attn, make_inputs,
+            WORKLOADS)
     if not args.no_proj and w.dtype != "fp32":
         print("bench: projection gradients ...", file=sys.stderr, flush=True)
         result["layer_proj"] = proj_bench(w, max(5, args.steps // 2), torch, attn)

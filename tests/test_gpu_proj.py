@@ -146,7 +146,8 @@ def test_projection_sizes_sampled():
         "dw_o": (to64(dw_o[rows_h]), o64[:, rows_h].T @ g64, W_TOL),
         "do_cat": (to64(do_cat[rows_t]), g64[rows_t] @ to64(Wo).T, OUT_TOL["bf16"]),
         "dw_q": (to64(pr["dw_q"][rows_w]), x64[:, rows_w].T @ to64(dQ), W_TOL),
-        "dw_v": (to64(pr["dw_v"][rows_w]), x64[:, rows_w].T @ to64(dV), W_TOL),
+        "dw_k": (to64(pr["dw_k"][rows_w]), x64[:, rows_w].T @ to64(dK), W_TOL),
+        "dw_v":(to64(pr["dw_v"][rows_w]), x64[:, rows_w].T @ to64(dV), W_TOL),
         "dx": (to64(pr["dx"][rows_t]),
                sum(to64(dP[rows_t]) @ to64(W).T for dP, W in ((dQ, Wq), (dK, Wk), (dV, Wv))),
                OUT_TOL["bf16"]),
