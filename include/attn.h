@@ -86,7 +86,9 @@ enum attn_status {
     ATTN_ECAUSAL_SHAPE = 2,   /* attn_fwd/attn_bwd: causal with n != m (mlgrind "Inputs") */
     ATTN_EUNSUPPORTED = 3,    /* dtype, (d, dv) pair or mask not built, or unknown flag bits */
     ATTN_EWORKSPACE = 4,      /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
-    ATTN_EHIP = 5             /* the HIP runtime refused a launch */
+    ATTN_EHIP = 5,            /* the HIP runtime refused a launch */
+    ATTN_ESCRATCH = 6         /* attn_bwd_ex_noalloc: the problem needs more scratch than
+                                 ATTN_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -192,6 +194,30 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 int B, int H, int n, int m, int d, int dv, float scale, int mask,
                 int layout, int dtype, int flags, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * attn_bwd_ex for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument.  The per-row D and rescaled LSE (and, in the
+ * atomic dQ mode, the float32 dQ accumulator) go to a static device array
+ * of ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it
+ * runs on until the process ends.  ATTN_DQ_AUTO is first resolved to the
+ * mode the library picks; a problem whose scratch (attn_bwd_workspace_bytes
+ * with that mode) exceeds the array returns ATTN_ESCRATCH before anything
+ * is enqueued.  Every call on a GPU shares that GPU's one array and leaves
+ * its contents there: calls that overlap on one GPU (different streams or
+ * host threads) race and give wrong results, so serialise them.  The first
+ * call on each device looks up the array's address (hipGetSymbolAddress,
+ * with that device current); no call allocates or frees memory.  Arguments,
+ * the current-device rule and the results are otherwise those of
+ * attn_bwd_ex.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int attn_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv_out,
+                        const int* seqlens_q, const int* seqlens_k,
+                        int B, int H, int n, int m, int d, int dv, float scale, int mask,
+                        int layout, int dtype, int flags, void* stream);
 
 /*
  * Projection gradients of the multi-head self-attention layer around the

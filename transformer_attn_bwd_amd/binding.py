@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 # Values of include/attn.h.
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
-ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(6)
+(ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP,
+ ATTN_ESCRATCH) = range(7)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 ATTN_DQ_AUTO, ATTN_DQ_ATOMIC, ATTN_DQ_SEPARATE = 0, 1, 2
 DQ_SPLIT_SHIFT, DQ_SPLIT_MAX = 12, 255
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
@@ -32,6 +34,7 @@ DQ_MODES = {"auto": ATTN_DQ_AUTO, "atomic": ATTN_DQ_ATOMIC, "separate": ATTN_DQ_
 STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
+            "attn_bwd_ex_noalloc",
             "attn_out_proj_bwd", "attn_in_proj_bwd", "attn_status_str", "attn_version")
 
 _lib = None
@@ -63,6 +66,8 @@ def load():
     lib.attn_fwd_ex.restype = I
     lib.attn_bwd_ex.argtypes = [vp] * 11 + [I] * 6 + [F, I, I, I, I, vp, Z, vp]
     lib.attn_bwd_ex.restype = I
+    lib.attn_bwd_ex_noalloc.argtypes = [vp] * 11 + [I] * 6 + [F, I, I, I, I, vp]
+    lib.attn_bwd_ex_noalloc.restype = I
     lib.attn_out_proj_bwd.argtypes = [vp] * 5 + [I] * 4 + [vp]
     lib.attn_out_proj_bwd.restype = I
     lib.attn_in_proj_bwd.argtypes = [vp] * 11 + [I] * 5 + [vp]
@@ -223,6 +228,37 @@ def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto")
     return int(load().attn_bwd_workspace_bytes(B, H, n, m, d, dv, code, _dq_flags(dq_mode, None)))
 
 
+def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, layout, dq_mode, dq_split, stages, scale):
+    """Checks shared by bwd and bwd_noalloc; returns the sizes, dtype code,
+    flags and scale."""
+    B, H, n, m, d, dvw = _shape(q, k, v, layout)
+    code = _dtype_code(q)
+    _expect(o, "o", _rows_shape(B, H, n, dvw, layout), q.dtype)
+    _expect(do, "do", _rows_shape(B, H, n, dvw, layout), q.dtype)
+    _expect(lse, "lse", (B, H, n), torch.float32)
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        if t is not None:
+            _expect(t, name, ref.shape, q.dtype)
+    flags = _dq_flags(dq_mode, dq_split)
+    _check_dev(q, k, v, o, do, lse)
+    _same_device(q, k, v, o, do, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stages:
+        for s_ in stages:
+            flags |= STAGES[s_]
+    return (B, H, n, m, d, dvw), code, flags, scale
+
+
+def _outputs(q, k, v, dq, dk, dv):
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_dev(dq, dk, dv)
+    _same_device(q, dq, dk, dv)
+    return dq, dk, dv
+
+
 def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace=None,
         dq=None, dk=None, dv=None, stages=None, mask=None, seqlens_q=None, seqlens_k=None,
         layout="bhsd", dq_split=None):
@@ -236,32 +272,16 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
     attn_bwd_ex, as in fwd().
     """
     lib = load()
-    B, H, n, m, d, dvw = _shape(q, k, v, layout)
-    code = _dtype_code(q)
-    _expect(o, "o", _rows_shape(B, H, n, dvw, layout), q.dtype)
-    _expect(do, "do", _rows_shape(B, H, n, dvw, layout), q.dtype)
-    _expect(lse, "lse", (B, H, n), torch.float32)
-    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-        if t is not None:
-            _expect(t, name, ref.shape, q.dtype)
     if workspace is not None and workspace.dtype != torch.uint8:
         raise TypeError(f"workspace must be torch.uint8, got {workspace.dtype}")
-    flags = _dq_flags(dq_mode, dq_split)
-    _check_dev(q, k, v, o, do, lse)
-    _same_device(q, k, v, o, do, lse)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if stages:
-        for s_ in stages:
-            flags |= STAGES[s_]
+    (B, H, n, m, d, dvw), code, flags, scale = _bwd_args(
+        q, k, v, o, do, lse, dq, dk, dv, layout, dq_mode, dq_split, stages, scale)
     need = int(lib.attn_bwd_workspace_bytes(B, H, n, m, d, dvw, code, flags))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    _check_dev(dq, dk, dv, workspace)
-    _same_device(q, dq, dk, dv, workspace)
+    _check_dev(workspace)
+    _same_device(q, workspace)
+    dq, dk, dv = _outputs(q, k, v, dq, dk, dv)
     ws_bytes = workspace.numel() * workspace.element_size()
     if mask is None and seqlens_q is None and seqlens_k is None and layout == "bhsd":
         st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
@@ -279,6 +299,31 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
         where = "attn_bwd_ex"
     if st != ATTN_OK:
         raise AttnError(st, where)
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, dq_mode="auto",
+                stages=None, mask=None, seqlens_q=None, seqlens_k=None, layout="bhsd",
+                dq_split=None):
+    """attn_bwd_ex_noalloc: the backward into the caller's dq, dk, dv with
+    the library's static per-GPU scratch instead of a workspace (no device
+    memory is allocated, here or in the library).  Calls that overlap on one
+    GPU share that scratch and race.  Arguments as in bwd()."""
+    lib = load()
+    if dq is None or dk is None or dv is None:
+        raise ValueError("bwd_noalloc writes into the caller's dq, dk and dv")
+    (B, H, n, m, d, dvw), code, flags, scale = _bwd_args(
+        q, k, v, o, do, lse, dq, dk, dv, layout, dq_mode, dq_split, stages, scale)
+    dq, dk, dv = _outputs(q, k, v, dq, dk, dv)
+    mcode = _mask_code(causal, mask)
+    sq, sk = _lens(seqlens_q, B), _lens(seqlens_k, B)
+    _same_device(q, *(t for t in (sq, sk) if t is not None))
+    st = lib.attn_bwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(sq), _ptr(sk), B, H, n, m,
+                                 d, dvw, float(scale), mcode, LAYOUTS[layout], code, flags,
+                                 _stream(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_ex_noalloc")
     return dq, dk, dv
 
 

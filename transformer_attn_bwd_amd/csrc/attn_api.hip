@@ -3,8 +3,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "attn.h"
 #include "attn_launch.h"
+
+// The no-allocation backward's scratch: one array per GPU, held for the
+// life of the process.  Host code never passes `scratch` itself to a kernel
+// (on the host it names a stand-in, not device memory); it passes the
+// device address that scratch_addr() looks up once per device.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -115,6 +124,34 @@ int resolve_dq(const Problem& p, int flags) {
     return -1;   // ATTN_DQ_AUTO
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+int scratch_addr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ATTN_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_EUNSUPPORTED;
+    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+                (void)hipGetLastError();
+                return ATTN_EHIP;
+            }
+            g_scratch_addr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return ATTN_OK;
+}
+
 int hip_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
@@ -202,6 +239,7 @@ const char* attn_status_str(int status) {
     case ATTN_EUNSUPPORTED: return "unsupported dtype, head widths, size or flags";
     case ATTN_EWORKSPACE: return "workspace missing or too small";
     case ATTN_EHIP: return "HIP launch failed";
+    case ATTN_ESCRATCH: return "problem needs more scratch than the no-allocation call's static array";
     default: return "unknown status";
     }
 }
@@ -345,6 +383,31 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
         if ((st = hip_status()) != ATTN_OK) return st;
     }
     return ATTN_OK;
+}
+
+int attn_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv_out,
+                        const int* seqlens_q, const int* seqlens_k, int B, int H, int n, int m,
+                        int d, int dv, float scale, int mask, int layout, int dtype, int flags,
+                        void* stream) {
+    Problem p;
+    int st = check_problem(B, H, n, m, d, dv, scale, mask, dtype, &p);
+    if (st != ATTN_OK) return st;
+    if (flags & ~(kDqModeMask | kStageMask | kSplitMask)) return ATTN_EUNSUPPORTED;
+    // ATTN_DQ_AUTO becomes the mode it resolves to, so that the size check
+    // counts the accumulator only when the atomic mode really runs.
+    if ((flags & kDqModeMask) == ATTN_DQ_AUTO) {
+        const int split = resolve_dq(p, flags);
+        flags &= ~(kDqModeMask | kSplitMask);
+        flags |= split < 0 ? ATTN_DQ_SEPARATE : (ATTN_DQ_ATOMIC | ATTN_DQ_SPLIT(split));
+    }
+    const size_t need = workspace_bytes(p, flags);
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ESCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_addr(&ws)) != ATTN_OK) return st;
+    return attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv_out, seqlens_q, seqlens_k, B, H, n, m,
+                       d, dv, scale, mask, layout, dtype, flags, ws, ATTN_NOALLOC_SCRATCH_BYTES,
+                       stream);
 }
 
 int attn_out_proj_bwd(const void* o_cat, const void* g, const void* w_o, float* dw_o,
