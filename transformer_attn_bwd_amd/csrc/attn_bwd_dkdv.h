@@ -597,6 +597,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         constexpr int W = decltype(W_)::value;
         constexpr int SW = W < D ? W : D;      // slab width: what the region holds
         constexpr int CH = SW / 8;             // 16-byte chunks per slab row
+        // Stores go through a buffer resource ending after key row m - 1; a
+        // chunk past the last key or past the row's wcols columns gets an
+        // offset beyond that end, and the hardware drops it (no branch).
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)(m * stride * 2));
 #pragma unroll
         for (int sl = 0; sl < W / SW; ++sl) {
 #pragma unroll
@@ -618,14 +622,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     }
                 }
             }
+            // every row read first, then every store: one wait for the reads
+            vec8<T> w8[CH];
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
                 const int lin = 64 * i + lane, row = lin / CH, chunk = lin % CH;
-                const vec8<T> w8 = *reinterpret_cast<const vec8<T>*>(
+                w8[i] = *reinterpret_cast<const vec8<T>*>(
                     reg + row * SW + 8 * (chunk ^ (row & (CH - 1))));
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int lin = 64 * i + lane, row = lin / CH, chunk = lin % CH;
                 const int key = kw0 + row, col = sl * SW + 8 * chunk;
-                if (key < m && col < wcols)
-                    *reinterpret_cast<vec8<T>*>(out + (long)key * stride + col) = w8;
+                const uint32_t byte_off =
+                    col < wcols ? (uint32_t)(((long)key * stride + col) * 2) : 0xFFFFFFF0u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w8[i]), ro,
+                                                       byte_off, 0, 0);
             }
         }
     };

@@ -350,7 +350,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // chunk swizzle by (row >> 1) & 7 keeps both the 16-byte writes (16
         // rows per lane group) and the row reads free of bank conflicts
         float* regf = reinterpret_cast<float*>(sE) + wave * 64 * 32;
-        float* acc_head = dqacc + bh * (long)n_pad * D;
+        const __amdgpu_buffer_rsrc_t racc =
+            make_rsrc(dqacc + bh * (long)n_pad * D, (uint32_t)(n_pad * D * 4));
 #pragma unroll
         for (int x = 0; x < D / 32; ++x) {
 #pragma unroll
@@ -364,19 +365,27 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                               acc[x][t][4 * vq + 3]};
                 }
             }
+            f32x4 w4[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int lin = 64 * i + lane, row = lin >> 3, chunk = lin & 7;
-                const f32x4 w4 = *reinterpret_cast<const f32x4*>(
+                w4[i] = *reinterpret_cast<const f32x4*>(
                     regf + row * 32 + 4 * (chunk ^ ((row >> 1) & 7)));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int lin = 64 * i + lane, row = lin >> 3, chunk = lin & 7;
                 const int query = i0 + (C::BM / 2) * (row / 32) + 32 * wave + row % 32;
-                if (query < n_pad)
-                    *reinterpret_cast<f32x4*>(acc_head + (long)query * D + 32 * x + 4 * chunk) = w4;
+                // rows at or past n_pad fall beyond the buffer and are dropped
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, w4[i]), racc,
+                    (uint32_t)(((long)query * D + 32 * x + 4 * chunk) * 4), 0, 0);
             }
         }
         return;
     }
     T* reg = sE + wave * 64 * 64;
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc(dq + hq.base, (uint32_t)(n * hq.stride * 2));
 #pragma unroll
     for (int sl = 0; sl < D / 64; ++sl) {
 #pragma unroll
@@ -395,15 +404,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 }
             }
         }
+        vec8<T> w8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int lin = 64 * i + lane, row = lin / 8, chunk = lin % 8;
-            const vec8<T> w8 =
-                *reinterpret_cast<const vec8<T>*>(reg + row * 64 + 8 * (chunk ^ (row & 7)));
+            w8[i] = *reinterpret_cast<const vec8<T>*>(reg + row * 64 + 8 * (chunk ^ (row & 7)));
+        }
+        // rows at or past n fall beyond the buffer, columns past dg get an
+        // offset beyond it: the hardware drops both
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int lin = 64 * i + lane, row = lin / 8, chunk = lin % 8;
             const int query = i0 + (C::BM / 2) * (row / 32) + 32 * wave + row % 32;
             const int col = 64 * sl + 8 * chunk;
-            if (query < n && col < dg)
-                *reinterpret_cast<vec8<T>*>(dq + hq.base + (long)query * hq.stride + col) = w8;
+            const uint32_t byte_off =
+                col < dg ? (uint32_t)(((long)query * hq.stride + col) * 2) : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w8[i]), rdq,
+                                                   byte_off, 0, 0);
         }
     }
 }
