@@ -94,11 +94,12 @@ struct DkdvSched {
     // slot ds_slot(i).
     static constexpr int p_slot(int i) { return J_DP + (i * 2 * KB) / 32; }
     static constexpr int ds_slot(int i) { return J_DV + (i * 4 * NXV) / 32; }
-    // statistics of row group vq (accumulator slots 4vq..4vq+3) are read
-    // two slots before the first element that needs them
+    // statistics of row group vq (accumulator slots 4vq..4vq+3): LSE2 is
+    // read two slots before the first element that needs it, -D (the
+    // starting value of the dP accumulators) four slots before dP
     static constexpr int first_elem_of_vq(int vq) { return 16 * (vq / 2) + 4 * (vq % 2); }
     static constexpr int l_slot(int vq) { return p_slot(first_elem_of_vq(vq)) - 2; }
-    static constexpr int d_slot(int vq) { return ds_slot(first_elem_of_vq(vq)) - 2; }
+    static constexpr int d_slot(int vq) { return J_DP - 4 + vq; }
 };
 
 // The dS tile of the fused dQ: 256 keys x 32 queries, 16-bit, one 64-byte
@@ -378,7 +379,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
         f32x16 S[2], dP[2];          // S is overwritten by P
         vec8<T> Pb[2][2], dSb[2][2];
-        f32x4 l4[4], d4[4];
+        f32x4 l4[4];
+        f32x16 nD;   // -D of the accumulator rows: slot 4vq + r is row 8vq + 4g + r
         vec8<T> fr[NF];
 
         // Query of accumulator slot e: i0 + 8(e>>2) + 4g + (e&3); key of
@@ -404,8 +406,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         };
         auto ds_elem = [&](auto i_) __attribute__((always_inline)) {
             constexpr int i = decltype(i_)::value;
-            constexpr int kt = SC::elem_kt(i), e = SC::elem_e(i), vq = e >> 2, r = e & 3;
-            dP[kt][e] = S[kt][e] * (dP[kt][e] - d4[vq][r]);
+            constexpr int kt = SC::elem_kt(i), e = SC::elem_e(i);
+            dP[kt][e] = S[kt][e] * dP[kt][e];   // dP already holds dO V^T - D
             if constexpr (i % 8 == 7) {
                 constexpr int c = SC::elem_c(i), b = 8 * c;
                 dSb[kt][c] = pack8<T>(dP[kt][b], dP[kt][b + 1], dP[kt][b + 2], dP[kt][b + 3],
@@ -471,8 +473,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 constexpr int vq = decltype(vq_)::value;
                 if constexpr (SC::l_slot(vq) == j)
                     l4[vq] = *reinterpret_cast<const f32x4*>(Ls + 8 * vq + 4 * g);
-                if constexpr (SC::d_slot(vq) == j)
-                    d4[vq] = *reinterpret_cast<const f32x4*>(Ds + 8 * vq + 4 * g);
+                if constexpr (SC::d_slot(vq) == j) {
+                    const f32x4 t4 = *reinterpret_cast<const f32x4*>(Ds + 8 * vq + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) nD[4 * vq + r] = t4[r];
+                }
             });
             // the product of this slot
             constexpr int kt = j % 2;
@@ -485,8 +490,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 S[kt] = mfma32(fr[r], fr[SC::F_K + kt * SC::KA + r], S[kt]);
             } else if constexpr (j < SC::J_DV) {
                 constexpr int r = (j - SC::J_DP) / 2;
-                if constexpr (r == 0) dP[kt] = zero16();
-                dP[kt] = mfma32(fr[SC::F_DO + r], vreg[kt][r], dP[kt]);
+                dP[kt] = mfma32(fr[SC::F_DO + r], vreg[kt][r], r == 0 ? nD : dP[kt]);
             } else if constexpr (j < SC::J_DK) {
                 constexpr int cx = (j - SC::J_DV) / 2, c = cx / SC::NXV, x = cx % SC::NXV;
                 mfma32_agpr(fr[SC::F_DOT + cx], Pb[kt][c], accV[kt][x]);

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         for (int kc = 0; kc < DV / 16; ++kc) asm volatile("" : "+a"(oreg[t][kc]));
         if (o == nullptr) {
             l2[t] = ok ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
-            Dq[t] = ok ? Dw[bh * (long)n_pad + myq[t]] : 0.f;
+            Dq[t] = ok ? -Dw[bh * (long)n_pad + myq[t]] : 0.f;   // the workspace holds -D
         }
     }
     if (o != nullptr) {
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             l2[t] = l > -INFINITY ? l * kLog2e : INFINITY;
             if (g == 0 && myq[t] < n_pad) {
                 lse2[bh * (long)n_pad + myq[t]] = l2[t];
-                Dw[bh * (long)n_pad + myq[t]] = Dq[t];
+                Dw[bh * (long)n_pad + myq[t]] = -Dq[t];
             }
         }
     }

@@ -4,8 +4,10 @@
 // attn_bwd_dq_mfma.hip).
 //
 // Preprocess: D_i = rowsum(dO o O)_i, the cheap form of rowsum(dP o P)
-// (step-by-step derivation, "Gradient of S"; mlgrind "Follow-up"), and LSE
-// rescaled to base 2 so that P = exp2(S * scale * log2e - LSE2).
+// (step-by-step derivation, "Gradient of S"; mlgrind "Follow-up"), stored
+// negated (the dK/dV kernel starts its dP accumulators from -D, so that
+// dS = P o (dP - D) is one multiply), and LSE rescaled to base 2 so that
+// P = exp2(S * scale * log2e - LSE2).
 #include "attn_bwd_dkdv.h"
 
 namespace attn {
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     if (valid_row && part == 0) {
         const float l = i < nb ? lse[bh * (long)n + i] : -INFINITY;
         lse2[row] = l > -INFINITY ? l * kLog2e : INFINITY;
-        Dw[row] = acc;
+        Dw[row] = -acc;
     }
 }
 
