@@ -41,8 +41,8 @@ KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip"
                   "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "7c90c0964c97c6b56e87ff4d5dbbd003c3ec7c4e1d43dd39522444875db6bdac",
-    "bytes": {"bwd_dkdv": 7.6320e+08},
+    "sources_sha256": "30ac5ccb614e4be2f479f131ddf72cf48beefa559dc37bf33c452a80428dfc00",
+    "bytes": {"bwd_dkdv": 7.6410e+08},
 }
 
 
