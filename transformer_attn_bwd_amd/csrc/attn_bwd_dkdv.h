@@ -167,7 +167,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         else return x1;
     };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform: the plain kernel computes it once into a
+    // scalar register, so that the LDS addresses of the tile fills (M0)
+    // need no per-load vector-to-scalar move.  The kernel with the fused dQ
+    // keeps it in a vector register: its scalar form gave wrong dK in the
+    // last step of some workgroups (GPU tests of the atomic mode), a
+    // miscompile or hazard not yet located.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = DQA ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
     const TileOrder to = tile_order((int)gridDim.x, (int)gridDim.y);
     const long bh = to.head;

@@ -71,7 +71,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         else return sV1;
     };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: computed once into a scalar register, so
+    // that the LDS addresses of the tile fills (M0) need no per-load
+    // vector-to-scalar move
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
     const TileOrder to = tile_order((int)gridDim.x, (int)gridDim.y);
     const long bh = to.head;

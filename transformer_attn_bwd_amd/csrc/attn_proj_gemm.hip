@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
     int mt, nt;
     if (!pick_tile(tm, tn, mt, nt)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: a scalar register
     const int g = lane >> 5, li = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = mt * GBM, n0 = nt * GBN;
@@ -199,7 +200,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
     int mt, nt;
     if (!pick_tile(tm, tn, mt, nt)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: a scalar register
     const int g = lane >> 5, li = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = mt * GBM, n0 = nt * GBN;
