@@ -5,10 +5,16 @@ The library is written next to this file so that it travels with the tree.
 """
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+try:
+    from .hazards import check_asm
+except ImportError:            # run as a script
+    from hazards import check_asm
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -45,16 +51,28 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def _compile(unit: tuple[str, str | None], extra: list[str]) -> str:
+def _compile(unit: tuple[str, str | None], extra: list[str]) -> tuple[str, list[str]]:
+    """Compile one unit; returns the object and the hazard-check findings
+    in its device assembly (kept, with -save-temps, in a directory of its
+    own under _build)."""
     src, elem = unit
     stem = os.path.splitext(src)[0] + (f"_{elem}" if elem else "")
     obj = os.path.join(OBJ_DIR, stem + ".o")
+    temps = os.path.join(OBJ_DIR, stem)
+    os.makedirs(temps, exist_ok=True)
     defs = [f"-DATTN_ELEM={elem}"] if elem else []
-    cmd = [hipcc(), *COMMON_FLAGS, *defs, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    cmd = [hipcc(), *COMMON_FLAGS, *defs, *extra, "-save-temps", "-c", os.path.join(CSRC, src),
+           "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=temps)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    return obj
+    findings = []
+    for asm in glob.glob(os.path.join(temps, f"*-hip-amdgcn-amd-amdhsa-{ARCH}.s")):
+        with open(asm) as f:
+            findings += [f"{os.path.relpath(asm, ROOT)}: {v}" for v in check_asm(f.read())]
+    for big in glob.glob(os.path.join(temps, "*.hipi")) + glob.glob(os.path.join(temps, "*.bc")):
+        os.remove(big)
+    return obj, findings
 
 
 def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
@@ -63,7 +81,12 @@ def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     workers = max(1, min(len(UNITS), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(lambda u: _compile(u, extra), UNITS))
+        done = list(ex.map(lambda u: _compile(u, extra), UNITS))
+    objs = [o for o, _ in done]
+    findings = [v for _, f in done for v in f]
+    if findings:
+        raise RuntimeError("AGPR accumulator read or written too soon after an inline-asm MFMA "
+                           "(see transformer_attn_bwd_amd/hazards.py):\n" + "\n".join(findings[:20]))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

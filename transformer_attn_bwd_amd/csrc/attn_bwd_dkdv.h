@@ -167,14 +167,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         else return x1;
     };
 
-    // The wave index is uniform: the plain kernel computes it once into a
-    // scalar register, so that the LDS addresses of the tile fills (M0)
-    // need no per-load vector-to-scalar move.  The kernel with the fused dQ
-    // keeps it in a vector register: its scalar form gave wrong dK in the
-    // last step of some workgroups (GPU tests of the atomic mode), a
-    // miscompile or hazard not yet located.
+    // the wave index is uniform: computed once into a scalar register, so
+    // that the LDS addresses of the tile fills (M0) need no per-load
+    // vector-to-scalar move
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = DQA ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, li = lane & 31;
     const TileOrder to = tile_order((int)gridDim.x, (int)gridDim.y);
     const long bh = to.head;
@@ -588,8 +585,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 
     // wait states between the last MFMA writing an accumulator and the
-    // reads below
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // reads below, and no read of an accumulator before them
+    mfma_agpr_wait();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) mfma_agpr_fence(accK[kt][x]);
+#pragma unroll
+        for (int x = 0; x < DV / 32; ++x) mfma_agpr_fence(accV[kt][x]);
+    }
 
     // The products were taken with the operands swapped, so the
     // accumulators hold dK^T and dV^T: slot vv of tile (kt, x) is column

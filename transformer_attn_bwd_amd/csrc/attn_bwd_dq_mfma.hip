@@ -342,8 +342,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if (s < nsteps) do_step(B0{}, MaskOn{}, s);
 
     // wait states between the last MFMA writing an accumulator and the
-    // reads below
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // reads below, and no read of an accumulator before them
+    mfma_agpr_wait();
+#pragma unroll
+    for (int x = 0; x < D / 32; ++x) {
+        mfma_agpr_fence(acc[x][0]);
+        mfma_agpr_fence(acc[x][1]);
+    }
     // Accumulator slot vv of tile (x, t) holds column d = 32x + 8(vv>>2) +
     // 4g + (vv&3) of query myq[t].  The tiles go out through this wave's
     // staging rows in LDS: written row-major (16-byte chunks XOR-swizzled by

@@ -66,13 +66,28 @@ __device__ __forceinline__ f32x16 mfma32(vec8<f16> a, vec8<f16> b, f32x16 c) {
 // file.  The compiler does not see these as MFMAs, so the hazards it
 // would cover are covered here: s_nop 1 gives the two wait states an MFMA
 // needs after a VALU write of its A or B operand; the accumulator is only
-// ever touched by this chain, and callers wait (s_nop) before reading it.
+// ever touched by this chain, and callers end the chain with
+// mfma_agpr_drain before anything else reads it.
 __device__ __forceinline__ void mfma32_agpr(vec8<bf16> a, vec8<bf16> b, f32x16& acc) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_agpr(vec8<f16> a, vec8<f16> b, f32x16& acc) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
+// Wait states between the last mfma32_agpr writing an accumulator and any
+// other read of it (24, more than the 18 a 32x32 MFMA result needs before a
+// VALU or v_accvgpr_read reads it).  A wait alone is not enough: the
+// compiler may schedule a register move of an accumulator (v_accvgpr_read)
+// anywhere after the last asm statement that names it, before the wait,
+// where it reads a value the MFMA has not written yet.  So each
+// accumulator passes through an asm statement placed after the wait
+// (volatile asm statements keep their order), and every read of it comes
+// after that.
+__device__ __forceinline__ void mfma_agpr_wait() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+__device__ __forceinline__ void mfma_agpr_fence(f32x16& acc) { asm volatile("" : "+a"(acc)); }
 
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;

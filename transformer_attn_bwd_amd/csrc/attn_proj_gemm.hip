@@ -64,7 +64,10 @@ __device__ __forceinline__ bool pick_tile(int tm, int tn, int& mt, int& nt) {
 template <typename OutT>
 __device__ __forceinline__ void store_block(OutT* c, long ldc, int M, int N, int row0, int col0,
                                             f32x16 (&acc)[4][4], int g, int li) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // (no per-accumulator fence here: it made the register allocator copy
+    // accumulators at the loop exit, before the wait; the build's hazard
+    // check confirms that every accumulator read follows the wait)
+    mfma_agpr_wait();
     OutT* base = c + (long)(row0 + 4 * g) * ldc + col0 + li;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
