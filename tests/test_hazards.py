@@ -61,3 +61,17 @@ def test_last_build_is_clean():
         with open(f) as fh:
             found += check_asm(fh.read())
     assert found == [], found[:5]
+
+
+def test_operand_written_just_before_the_mfma_is_reported():
+    asm = HEAD + "\tv_cvt_pk_bf16_f32 v5, v10, v11\n" + MFMA + WAIT + END
+    v = check_asm(asm)
+    assert len(v) == 1 and "v5" in v[0]
+
+
+def test_operand_written_two_wait_states_before_passes():
+    asm = HEAD + "\tv_cvt_pk_bf16_f32 v5, v10, v11\n\ts_nop 1\n" + MFMA + WAIT + END
+    assert check_asm(asm) == []
+    asm = HEAD + "\tv_cvt_pk_bf16_f32 v5, v10, v11\n\tv_add_f32_e32 v20, v21, v22\n" \
+        "\ts_add_i32 s0, s0, 1\n" + MFMA + WAIT + END
+    assert check_asm(asm) == []

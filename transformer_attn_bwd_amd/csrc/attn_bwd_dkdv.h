@@ -140,6 +140,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     float scale, float c2, SeqInfo si) {
     using C = DkdvCfg<D, DV>;
     using SC = DkdvSched<D, DV>;
+    // the 128/128 kernel without the fused dQ forms P and dS slots before
+    // the products that read them (checked in the assembly at build time)
+    constexpr bool kOperandWait = DQA || D != 128 || DV != 128;
     constexpr int BM = C::BM, NW = C::NW, LA = C::LA;
     // One LDS variable per buffer: the compiler can then tell that reads
     // of one buffer do not alias the asynchronous fills of the other, and
@@ -497,10 +500,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 dP[kt] = mfma32(fr[SC::F_DO + r], vreg[kt][r], r == 0 ? nD : dP[kt]);
             } else if constexpr (j < SC::J_DK) {
                 constexpr int cx = (j - SC::J_DV) / 2, c = cx / SC::NXV, x = cx % SC::NXV;
-                mfma32_agpr(fr[SC::F_DOT + cx], Pb[kt][c], accV[kt][x]);
+                mfma32_agpr<kOperandWait>(fr[SC::F_DOT + cx], Pb[kt][c], accV[kt][x]);
             } else {
                 constexpr int cx = (j - SC::J_DK) / 2, c = cx / SC::NX, x = cx % SC::NX;
-                mfma32_agpr(fr[SC::F_QT + cx], dSb[kt][c], accK[kt][x]);
+                mfma32_agpr<kOperandWait>(fr[SC::F_QT + cx], dSb[kt][c], accK[kt][x]);
                 if constexpr (DQA) {
                     constexpr int t = j - SC::J_DK;
                     if constexpr (t < 4) {

@@ -53,6 +53,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     float scale, float c2, SeqInfo si) {
     using C = DqCfg<D, DV>;
     constexpr int BN = C::BN, PD = C::PD, NW = C::NW;
+    // the d = 128 kernels form dS a fragment before the products that read
+    // it (checked in the assembly at build time)
+    constexpr bool kOperandWait = D != 128;
     // One LDS variable per buffer: the compiler can then tell that reads
     // of one buffer do not alias the asynchronous fills of the other, and
     // does not make them wait for those fills.
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 constexpr int cx = f - FT, c = cx / NX, x = cx % NX;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    mfma32_agpr(cur, dSb[c / 2][t][c % 2], acc[x][t]);
+                    mfma32_agpr<kOperandWait>(cur, dSb[c / 2][t][c % 2], acc[x][t]);
                 });
                 // dS of chunk c + 1 during the products of chunk c
                 if constexpr (c + 1 < NC && x == 0)

@@ -63,16 +63,26 @@ __device__ __forceinline__ f32x16 mfma32(vec8<f16> a, vec8<f16> b, f32x16 c) {
 // The same products with the accumulator pinned in AGPRs, for kernels whose
 // accumulators do not fit next to their other operands in the 256 VGPRs.
 // Written out because the compiler places all MFMA results in one register
-// file.  The compiler does not see these as MFMAs, so the hazards it
-// would cover are covered here: s_nop 1 gives the two wait states an MFMA
-// needs after a VALU write of its A or B operand; the accumulator is only
-// ever touched by this chain, and callers end the chain with
-// mfma_agpr_drain before anything else reads it.
+// file.  The compiler does not see these as MFMAs, so it inserts none of
+// the wait states an MFMA needs around it: the two after a VALU write of
+// its A or B operand, given here by an s_nop 1 unless the caller's schedule
+// keeps such writes two instructions away by itself (WAIT = false, used
+// where the build's hazard check finds it so in the assembly; it fails the
+// build otherwise), and the 18 before anything else reads the accumulator
+// (callers end the chain with mfma_agpr_wait and mfma_agpr_fence).
+template <bool WAIT = true>
 __device__ __forceinline__ void mfma32_agpr(vec8<bf16> a, vec8<bf16> b, f32x16& acc) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    if constexpr (WAIT)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+template <bool WAIT = true>
 __device__ __forceinline__ void mfma32_agpr(vec8<f16> a, vec8<f16> b, f32x16& acc) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    if constexpr (WAIT)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Wait states between the last mfma32_agpr writing an accumulator and any

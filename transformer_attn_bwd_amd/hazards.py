@@ -10,21 +10,41 @@ allocator may still place a copy of an accumulator (``v_accvgpr_read``,
 loop exit.  Such a copy reads a value the MFMA has not written yet, and the
 result is silently wrong.
 
+The same blindness applies in the other direction: an MFMA needs two wait
+states after a VALU instruction writes one of its A or B operands, which
+the compiler would insert before its own MFMAs but not before the asm.
+
 ``check_asm`` builds each kernel's control-flow graph from the assembly
-text and computes, at every instruction, the fewest wait states since an
-MFMA with an AGPR destination along any path (an ``s_nop N`` gives N + 1,
-any other instruction one, MFMAs none); an instruction other than an MFMA
-that names an AGPR with fewer than 18 is reported.
+text and computes, at every instruction, the fewest wait states along any
+path (an ``s_nop N`` gives N + 1, any other instruction one, MFMAs none)
+since an MFMA with an AGPR destination, and since the last VALU write of
+each VGPR.  It reports an instruction other than an MFMA that names an
+AGPR with fewer than 18 of the first, and an AGPR-destination MFMA that
+reads a VGPR with fewer than 2 of the second.
 """
 from __future__ import annotations
 
 import re
 
 WAIT_STATES = 18
+OPERAND_WAIT_STATES = 2
 INF = 1 << 30
 _KERNEL = re.compile(r"^(_Z\S+):")
 _LABEL = re.compile(r"^(\.L\S+):")
 _AGPR = re.compile(r"\ba(\d+)\b|\ba\[\d+:\d+\]")
+_VREG = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
+# VALU instructions whose destination is not a VGPR, or that are not VALU
+_NOT_VGPR_WRITERS = ("v_cmp", "v_cmpx", "v_readfirstlane", "v_readlane", "v_accvgpr_write",
+                     "v_mfma")
+
+
+def _vregs(tok: str) -> set[int]:
+    m = _VREG.match(tok.strip())
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
 
 
 def _kernels(text: str):
@@ -84,20 +104,47 @@ def _blocks(body):
     return blocks, succ
 
 
-def _run(ins, w, report):
+def _age(recent, k):
+    """Advance the VGPR write ages by k wait states, dropping old ones."""
+    return {r: a + k for r, a in recent.items() if a + k < OPERAND_WAIT_STATES}
+
+
+def _run(ins, state, report):
+    w, recent = state
     for lineno, s in ins:
         op = s.split()[0]
         if op.startswith("v_mfma"):
-            if s.split(None, 1)[1].split(",")[0].strip().startswith("a"):
+            ops = [o.strip() for o in s.split(None, 1)[1].split(",")]
+            if ops[0].startswith("a"):
+                for r in _vregs(ops[1]) | _vregs(ops[2]):
+                    if r in recent:
+                        report.append((lineno, s, f"v{r} written {recent[r]} wait states before "
+                                                   f"this MFMA reads it"))
                 w = 0
             continue
         if op == "s_nop":
-            w = min(INF, w + int(s.split()[1], 0) + 1)
+            k = int(s.split()[1], 0) + 1
+            w = min(INF, w + k)
+            recent = _age(recent, k)
             continue
         if w < WAIT_STATES and _AGPR.search(s):
-            report.append((lineno, s, w))
+            report.append((lineno, s, f"{w} wait states after an AGPR-accumulating MFMA"))
         w = min(INF, w + 1)
-    return w
+        recent = _age(recent, 1)
+        if op.startswith("v_") and not op.startswith(_NOT_VGPR_WRITERS):
+            parts = s.split(None, 1)
+            if len(parts) > 1:
+                for r in _vregs(parts[1].split(",")[0]):
+                    recent[r] = 0
+    return w, recent
+
+
+def _merge(a, b):
+    """State at a join: the fewest wait states on either path."""
+    recent = dict(a[1])
+    for r, age in b[1].items():
+        recent[r] = min(age, recent.get(r, age))
+    return min(a[0], b[0]), recent
 
 
 def check_asm(text: str) -> list[str]:
@@ -107,22 +154,22 @@ def check_asm(text: str) -> list[str]:
         blocks, succ = _blocks(body)
         if not blocks:
             continue
-        entry = [INF] * len(blocks)
+        entry = [None] * len(blocks)
+        entry[0] = (INF, {})
         work = [0]
-        seen = set()
         while work:
             i = work.pop()
-            seen.add(i)
-            w = _run(blocks[i][1], entry[i], [])
+            st = _run(blocks[i][1], entry[i], [])
             for j in succ[i]:
-                if w < entry[j] or j not in seen:
-                    entry[j] = min(entry[j], w)
-                    seen.add(j)
+                new = st if entry[j] is None else _merge(entry[j], st)
+                if entry[j] is None or new != entry[j]:
+                    entry[j] = new
                     work.append(j)
         for i, (_, ins) in enumerate(blocks):
+            if entry[i] is None:
+                continue
             rep = []
             _run(ins, entry[i], rep)
-            for lineno, s, w in rep:
-                out.append(f"{name}: line {lineno}: '{s}' {w} wait states after an "
-                           f"AGPR-accumulating MFMA")
+            for lineno, s, why in rep:
+                out.append(f"{name}: line {lineno}: '{s}': {why}")
     return out
