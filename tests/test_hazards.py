@@ -75,3 +75,11 @@ def test_operand_written_two_wait_states_before_passes():
     asm = HEAD + "\tv_cvt_pk_bf16_f32 v5, v10, v11\n\tv_add_f32_e32 v20, v21, v22\n" \
         "\ts_add_i32 s0, s0, 1\n" + MFMA + WAIT + END
     assert check_asm(asm) == []
+
+
+def test_other_agprs_are_free_right_after_the_mfma():
+    # a20 is not written by the MFMA (a value the compiler parked in an AGPR)
+    asm = HEAD + MFMA + "\tv_accvgpr_read_b32 v8, a20\n\tv_accvgpr_write_b32 a16, v9\n" + WAIT + END
+    assert check_asm(asm) == []
+    asm = HEAD + MFMA + "\tv_accvgpr_read_b32 v8, a15\n" + WAIT + END
+    assert len(check_asm(asm)) == 1

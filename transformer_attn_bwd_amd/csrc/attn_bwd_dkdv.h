@@ -608,17 +608,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // rows per instruction.  Keys past mb are padding: zeros, selected rather
     // than multiplied, since a padded key's accumulators may hold inf (S = 0
     // there, and P = exp2(-LSE2) overflows when a row's LSE is very
-    // negative).
+    // negative).  Only a wave whose 64 keys reach past mb takes the
+    // selecting copy of the epilogue.
     T* reg = sK + C::KW * wave * D;
-    auto put_tile = [&](auto W_, const f32x16 (&acc)[2][W_.value / 32], int wcols, float mult,
-                        T* out, long stride) __attribute__((always_inline)) {
+    auto put_tile = [&](auto W_, auto RAGGED_, const f32x16 (&acc)[2][W_.value / 32], int wcols,
+                        float mult, T* out, long stride) __attribute__((always_inline)) {
         constexpr int W = decltype(W_)::value;
+        constexpr bool RAGGED = decltype(RAGGED_)::value;
         constexpr int SW = W < D ? W : D;      // slab width: what the region holds
         constexpr int CH = SW / 8;             // 16-byte chunks per slab row
+        constexpr int RPI = 64 / CH;           // rows per store instruction
         // Stores go through a buffer resource ending after key row m - 1; a
         // chunk past the last key or past the row's wcols columns gets an
         // offset beyond that end, and the hardware drops it (no branch).
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (uint32_t)(m * stride * 2));
+        // lane's row and chunk in store i: row RPI i + lane / CH, chunk lane % CH
+        const int srow = lane / CH, schunk = lane % CH;
+        const uint32_t row_step = (uint32_t)(RPI * stride * 2);
 #pragma unroll
         for (int sl = 0; sl < W / SW; ++sl) {
 #pragma unroll
@@ -632,8 +638,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     for (int vq = 0; vq < 4; ++vq) {
                         vec4<T> w4;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            w4[r] = real ? (T)(acc[kt][x][4 * vq + r] * mult) : (T)0.f;
+                        for (int r = 0; r < 4; ++r) w4[r] = (T)(acc[kt][x][4 * vq + r] * mult);
+                        if constexpr (RAGGED) {
+                            u32x2 b = __builtin_bit_cast(u32x2, w4);
+                            b = real ? b : u32x2{0u, 0u};
+                            w4 = __builtin_bit_cast(vec4<T>, b);
+                        }
                         const int chunk = 4 * xs + vq;
                         *reinterpret_cast<vec4<T>*>(
                             reg + row * SW + 8 * (chunk ^ (row & (CH - 1))) + 4 * g) = w4;
@@ -644,23 +654,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             vec8<T> w8[CH];
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                const int lin = 64 * i + lane, row = lin / CH, chunk = lin % CH;
+                const int row = RPI * i + srow;
                 w8[i] = *reinterpret_cast<const vec8<T>*>(
-                    reg + row * SW + 8 * (chunk ^ (row & (CH - 1))));
+                    reg + row * SW + 8 * (schunk ^ (row & (CH - 1))));
             }
+            const int col = sl * SW + 8 * schunk;
+            const uint32_t off0 = (uint32_t)(((long)(kw0 + srow) * stride + col) * 2);
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                const int lin = 64 * i + lane, row = lin / CH, chunk = lin % CH;
-                const int key = kw0 + row, col = sl * SW + 8 * chunk;
-                const uint32_t byte_off =
-                    col < wcols ? (uint32_t)(((long)key * stride + col) * 2) : 0xFFFFFFF0u;
+                const uint32_t byte_off = col < wcols ? off0 + (uint32_t)i * row_step : 0xFFFFFFF0u;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w8[i]), ro,
                                                        byte_off, 0, 0);
             }
         }
     };
-    put_tile(std::integral_constant<int, D>{}, accK, dg, scale, dk + hk.base, hk.stride);
-    put_tile(std::integral_constant<int, DV>{}, accV, dvg, 1.f, dvo + hv.base, hv.stride);
+    using Dc = std::integral_constant<int, D>;
+    using DVc = std::integral_constant<int, DV>;
+    if (kw0 + C::KW <= mb) {
+        put_tile(Dc{}, std::false_type{}, accK, dg, scale, dk + hk.base, hk.stride);
+        put_tile(DVc{}, std::false_type{}, accV, dvg, 1.f, dvo + hv.base, hv.stride);
+    } else {
+        put_tile(Dc{}, std::true_type{}, accK, dg, scale, dk + hk.base, hk.stride);
+        put_tile(DVc{}, std::true_type{}, accV, dvg, 1.f, dvo + hv.base, hv.stride);
+    }
 }
 
 template <typename T, int D, int DV, bool DQA>

@@ -103,13 +103,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Taking one tile from each half of the workgroup's rows gives every
     // wave the same share of the masked diagonal work.  Rows past nb load
     // zeros and LSE2 = +inf, so their P, dS and dQ vanish.
+    //
+    // Every load of the prologue (Q and dO rows, the O rows and LSE of the
+    // preprocess or the workspace's LSE2 and -D, and the first K and V tile)
+    // is issued before anything waits for one, so that their latencies
+    // overlap instead of adding up.
     int myq[2];
+    bool okq[2];
     vec8<T> qreg[2][D / 16], oreg[2][DV / 16];
-    float l2[2], Dq[2];
+    float l2[2], nD[2];   // LSE2 and -D of the row
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         myq[t] = i0 + (C::BM / 2) * t + 32 * wave + li;
-        const bool ok = myq[t] < nb;
+        const bool ok = okq[t] = myq[t] < nb;
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc)
             qreg[t][kc] = (ok && 16 * kc + 8 * g < dg)
@@ -120,61 +126,28 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             oreg[t][kc] = (ok && 16 * kc + 8 * g < dvg)
                               ? gload8(oh + (long)myq[t] * ho.stride + 16 * kc + 8 * g)
                               : vec8<T>{};
-        // Q and dO rows are only MFMA inputs: keep them in AGPRs, leaving
-        // the VGPRs to the S, dP and dS tiles of a 64-key step
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) asm volatile("" : "+a"(qreg[t][kc]));
-#pragma unroll
-        for (int kc = 0; kc < DV / 16; ++kc) asm volatile("" : "+a"(oreg[t][kc]));
-        if (o == nullptr) {
-            l2[t] = ok ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
-            Dq[t] = ok ? -Dw[bh * (long)n_pad + myq[t]] : 0.f;   // the workspace holds -D
-        }
     }
+    vec8<T> orow[2][DV / 16];
+    float lraw[2];
     if (o != nullptr) {
-        // The preprocess for this workgroup's rows, in the arithmetic order
-        // of bwd_preprocess_kernel, so that both give the same bits: each
-        // 8-column chunk c summed in order, then the chunks pairwise at
-        // distances 8, 4, 2, 1 (16 chunks; 4, 2, 1 for 8).  This lane holds
-        // the chunks c = 2 kc + g, so the last step is the exchange with the
-        // lane 32 away.  Rows past nb get D = 0 and LSE2 = +inf, rows that
-        // saw no key (LSE = -inf) LSE2 = +inf.
         const HeadView hov = head_view(si, bh, n, dvg);
         const T* orow0 = o + hov.base;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const bool ok = myq[t] < nb;
-            float sc[DV / 16];
 #pragma unroll
-            for (int kc = 0; kc < DV / 16; ++kc) {
-                const bool in = ok && 16 * kc + 8 * g < dvg;
-                const vec8<T> a =
-                    in ? gload8(orow0 + (long)myq[t] * hov.stride + 16 * kc + 8 * g) : vec8<T>{};
-                const vec8<T> b = oreg[t][kc];
-                float acc = 0.f;
+            for (int kc = 0; kc < DV / 16; ++kc)
+                orow[t][kc] = (okq[t] && 16 * kc + 8 * g < dvg)
+                                  ? gload8(orow0 + (long)myq[t] * hov.stride + 16 * kc + 8 * g)
+                                  : vec8<T>{};
+            lraw[t] = okq[t] ? lse[bh * (long)n + myq[t]] : -INFINITY;
+        }
+    } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
-                sc[kc] = acc;
-            }
-#pragma unroll
-            for (int w = DV / 32; w >= 1; w /= 2) {
-#pragma unroll
-                for (int kc = 0; kc < w; ++kc) sc[kc] = sc[kc] + sc[kc + w];
-            }
-            Dq[t] = sc[0] + xor_lane32(sc[0]);
-            const float l = ok ? lse[bh * (long)n + myq[t]] : -INFINITY;
-            l2[t] = l > -INFINITY ? l * kLog2e : INFINITY;
-            if (g == 0 && myq[t] < n_pad) {
-                lse2[bh * (long)n_pad + myq[t]] = l2[t];
-                Dw[bh * (long)n_pad + myq[t]] = -Dq[t];
-            }
+        for (int t = 0; t < 2; ++t) {
+            l2[t] = okq[t] ? lse2[bh * (long)n_pad + myq[t]] : INFINITY;
+            nD[t] = okq[t] ? Dw[bh * (long)n_pad + myq[t]] : 0.f;   // the workspace holds -D
         }
     }
-
-    TileOffsets<D> toK;
-    toK.init(lane);
-    TileOffsets<DV> toV;
-    toV.init(lane);
 
     int k_end = CAUSAL ? min(mb, i0 + C::BM + off) : mb;
     if (i0 >= nb) k_end = 0;
@@ -198,6 +171,58 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         tile_fill<D, BN, NW>(ldK, Kbuf(buf_), rK, k0, wave);
         tile_fill<DV, BN, NW>(ldV, Vbuf(buf_), rV, k0, wave);
     };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if (nsteps > 0) stage(B0{}, 0);
+
+    if (o != nullptr) {
+        // The preprocess for this workgroup's rows, in the arithmetic order
+        // of bwd_preprocess_kernel, so that both give the same bits: each
+        // 8-column chunk c summed in order, then the chunks pairwise at
+        // distances 8, 4, 2, 1 (16 chunks; 4, 2, 1 for 8).  This lane holds
+        // the chunks c = 2 kc + g, so the last step is the exchange with the
+        // lane 32 away.  Rows past nb get D = 0 and LSE2 = +inf, rows that
+        // saw no key (LSE = -inf) LSE2 = +inf.
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            float sc[DV / 16];
+#pragma unroll
+            for (int kc = 0; kc < DV / 16; ++kc) {
+                const vec8<T> a = orow[t][kc];
+                const vec8<T> b = oreg[t][kc];
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+                sc[kc] = acc;
+            }
+#pragma unroll
+            for (int w = DV / 32; w >= 1; w /= 2) {
+#pragma unroll
+                for (int kc = 0; kc < w; ++kc) sc[kc] = sc[kc] + sc[kc + w];
+            }
+            nD[t] = -(sc[0] + xor_lane32(sc[0]));
+            const float l = lraw[t];
+            l2[t] = l > -INFINITY ? l * kLog2e : INFINITY;
+            if (g == 0 && myq[t] < n_pad) {
+                lse2[bh * (long)n_pad + myq[t]] = l2[t];
+                Dw[bh * (long)n_pad + myq[t]] = nD[t];
+            }
+        }
+    }
+    // Q and dO rows are only MFMA inputs: keep them in AGPRs, leaving the
+    // VGPRs to the S, dP and dS tiles of a 64-key step
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) asm volatile("" : "+a"(qreg[t][kc]));
+#pragma unroll
+        for (int kc = 0; kc < DV / 16; ++kc) asm volatile("" : "+a"(oreg[t][kc]));
+    }
+
+    TileOffsets<D> toK;
+    toK.init(lane);
+    TileOffsets<DV> toV;
+    toV.init(lane);
 
     f32x16 acc[D / 32][2];
 #pragma unroll
@@ -262,7 +287,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             float d8[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                d8[s] = S[kh][t][8 * h + s] * (dP[kh][t][8 * h + s] - Dq[t]);
+                d8[s] = S[kh][t][8 * h + s] * (dP[kh][t][8 * h + s] + nD[t]);
             dSb[kh][t][h] = pack8<T>(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
         };
 
@@ -313,8 +338,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         });
     };
 
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
     using MaskOn = std::integral_constant<bool, true>;
     using MaskOff = std::integral_constant<bool, false>;
 
@@ -327,7 +350,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         __syncthreads();
     };
 
-    if (nsteps > 0) stage(B0{}, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 

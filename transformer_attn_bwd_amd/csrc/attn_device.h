@@ -38,6 +38,7 @@ using vec4 = T __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Calls f(std::integral_constant<int, I>{}) for I = 0..N-1, so that every
 // index inside f is a compile-time constant (register arrays stay arrays).

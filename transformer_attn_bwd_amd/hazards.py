@@ -17,10 +17,12 @@ the compiler would insert before its own MFMAs but not before the asm.
 ``check_asm`` builds each kernel's control-flow graph from the assembly
 text and computes, at every instruction, the fewest wait states along any
 path (an ``s_nop N`` gives N + 1, any other instruction one, MFMAs none)
-since an MFMA with an AGPR destination, and since the last VALU write of
-each VGPR.  It reports an instruction other than an MFMA that names an
-AGPR with fewer than 18 of the first, and an AGPR-destination MFMA that
-reads a VGPR with fewer than 2 of the second.
+since an MFMA with an AGPR destination last wrote each AGPR, and since the
+last VALU write of each VGPR.  It reports an instruction other than an
+MFMA that names an AGPR some MFMA wrote fewer than 18 wait states before
+(other AGPRs, such as those the compiler uses to hold spilled values, are
+free to use), and an AGPR-destination MFMA that reads a VGPR with fewer
+than 2 of the second.
 """
 from __future__ import annotations
 
@@ -28,10 +30,9 @@ import re
 
 WAIT_STATES = 18
 OPERAND_WAIT_STATES = 2
-INF = 1 << 30
 _KERNEL = re.compile(r"^(_Z\S+):")
 _LABEL = re.compile(r"^(\.L\S+):")
-_AGPR = re.compile(r"\ba(\d+)\b|\ba\[\d+:\d+\]")
+_AGPR = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
 _VREG = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
 # VALU instructions whose destination is not a VGPR, or that are not VALU
 _NOT_VGPR_WRITERS = ("v_cmp", "v_cmpx", "v_readfirstlane", "v_readlane", "v_accvgpr_write",
@@ -104,13 +105,25 @@ def _blocks(body):
     return blocks, succ
 
 
-def _age(recent, k):
-    """Advance the VGPR write ages by k wait states, dropping old ones."""
-    return {r: a + k for r, a in recent.items() if a + k < OPERAND_WAIT_STATES}
+def _age(ages, k, limit):
+    """Advance the ages (wait states) by k, dropping those that reach limit."""
+    return {r: a + k for r, a in ages.items() if a + k < limit}
+
+
+def _agprs(text: str) -> set[int]:
+    out = set()
+    for m in _AGPR.finditer(text):
+        if m.group(1) is not None:
+            out.add(int(m.group(1)))
+        else:
+            out.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    return out
 
 
 def _run(ins, state, report):
-    w, recent = state
+    """state: (AGPR -> wait states since an MFMA wrote it, VGPR -> wait
+    states since a VALU wrote it), both holding only the recent ones."""
+    acc, recent = state
     for lineno, s in ins:
         op = s.split()[0]
         if op.startswith("v_mfma"):
@@ -120,31 +133,39 @@ def _run(ins, state, report):
                     if r in recent:
                         report.append((lineno, s, f"v{r} written {recent[r]} wait states before "
                                                    f"this MFMA reads it"))
-                w = 0
+                acc = dict(acc)
+                for r in _agprs(ops[0]):
+                    acc[r] = 0
             continue
         if op == "s_nop":
             k = int(s.split()[1], 0) + 1
-            w = min(INF, w + k)
-            recent = _age(recent, k)
+            acc = _age(acc, k, WAIT_STATES)
+            recent = _age(recent, k, OPERAND_WAIT_STATES)
             continue
-        if w < WAIT_STATES and _AGPR.search(s):
-            report.append((lineno, s, f"{w} wait states after an AGPR-accumulating MFMA"))
-        w = min(INF, w + 1)
-        recent = _age(recent, 1)
+        if acc:
+            hit = sorted(r for r in _agprs(s) if r in acc)
+            if hit:
+                report.append((lineno, s, f"a{hit[0]} written by an MFMA {acc[hit[0]]} wait "
+                                          f"states before"))
+        acc = _age(acc, 1, WAIT_STATES)
+        recent = _age(recent, 1, OPERAND_WAIT_STATES)
         if op.startswith("v_") and not op.startswith(_NOT_VGPR_WRITERS):
             parts = s.split(None, 1)
             if len(parts) > 1:
                 for r in _vregs(parts[1].split(",")[0]):
                     recent[r] = 0
-    return w, recent
+    return acc, recent
 
 
 def _merge(a, b):
     """State at a join: the fewest wait states on either path."""
-    recent = dict(a[1])
-    for r, age in b[1].items():
-        recent[r] = min(age, recent.get(r, age))
-    return min(a[0], b[0]), recent
+    out = []
+    for x, y in zip(a, b):
+        m = dict(x)
+        for r, age in y.items():
+            m[r] = min(age, m.get(r, age))
+        out.append(m)
+    return tuple(out)
 
 
 def check_asm(text: str) -> list[str]:
@@ -155,7 +176,7 @@ def check_asm(text: str) -> list[str]:
         if not blocks:
             continue
         entry = [None] * len(blocks)
-        entry[0] = (INF, {})
+        entry[0] = ({}, {})
         work = [0]
         while work:
             i = work.pop()
