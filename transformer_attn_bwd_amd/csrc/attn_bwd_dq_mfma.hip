@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             float d8[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                d8[s] = S[kh][t][8 * h + s] * (dP[kh][t][8 * h + s] + nD[t]);
+                d8[s] = S[kh][t][8 * h + s] * dP[kh][t][8 * h + s];
             dSb[kh][t][h] = pack8<T>(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
         };
 
@@ -310,8 +310,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 constexpr int kh = (f - FV) / KB, r = (f - FV) % KB;
                 static_for<2>([&](auto t_) {
                     constexpr int t = decltype(t_)::value;
-                    if constexpr (r == 0) dP[kh][t] = zero16();
-                    dP[kh][t] = mfma32(cur, oreg[t][r], dP[kh][t]);
+                    // dP^T starts at -D: every slot of this lane is query myq[t]
+                    if constexpr (r == 0) {
+                        f32x16 start;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) start[e] = nD[t];
+                        dP[kh][t] = mfma32(cur, oreg[t][0], start);
+                    } else {
+                        dP[kh][t] = mfma32(cur, oreg[t][r], dP[kh][t]);
+                    }
                 });
                 // 32 NKH exponentials over the NKH KB dP slots
                 static_for<32 * NKH>([&](auto i_) {
