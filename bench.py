@@ -41,8 +41,8 @@ KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip"
                   "attn_launch.h")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "f5b86a777b846f5c4a13d3f89344de7bd915e0ee14b3b77d643451775ee0be89",
-    "bytes": {"bwd_dkdv": 7.6133e+08},
+    "sources_sha256": "c2def514fbd27039f477b308b003ce60067159eaae88fb23018064a96f0df8e0",
+    "bytes": {"bwd_dkdv": 7.6574e+08},
 }
 
 
