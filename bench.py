@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # hold only for the kernel sources they were taken on, identified by hash;
 # after any change to those sources the traffic is reported as null.
 KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip", "attn_device.h",
-                  "attn_launch.h")
+                  "attn_launch.h", "attn_bwd_dkdv_dss.hip", "attn_bwd_dq_ds.hip")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
     "sources_sha256": "c2def514fbd27039f477b308b003ce60067159eaae88fb23018064a96f0df8e0",
@@ -82,6 +82,47 @@ def dq_flops(w) -> float:
     # S, dP recomputed, dQ += dS K
     f = 2.0 * w.n * w.m * (2 * w.d + w.dv) * w.B * w.H
     return f / 2 if w.causal else f
+
+
+def dq_ds_flops(w) -> float:
+    # dQ += dS K from the stored dS: the one product of the five left to it
+    f = 2.0 * w.n * w.m * w.d * w.B * w.H
+    return f / 2 if w.causal else f
+
+
+def ds_tile_bytes(w) -> float:
+    """Bytes of the stored-dS mode's dS tiles (16-bit, 256 x 256 each: the
+    diagonal and lower tiles under the causal mask, all without it)."""
+    nb, mb = -(-w.n // 256), -(-w.m // 256)
+    tiles = nb * (nb + 1) // 2 if w.causal else nb * mb
+    return float(w.B * w.H * tiles * 256 * 256 * 2)
+
+
+def dq_ds_bytes(w) -> float:
+    """Algorithmic HBM bytes of the dQ-from-dS pass: read the dS tiles and K
+    (16-bit); write dQ (16-bit)."""
+    return ds_tile_bytes(w) + float(w.B * w.H * (w.m * w.d + w.n * w.d) * 2)
+
+
+def mode_kernels(w, mode):
+    """(FLOPs, algorithmic bytes) of the dK/dV and dQ kernels in a dQ mode
+    (the atomic mode's are set by its split, in mode_figures)."""
+    if mode == "stored_ds":
+        return {"dkdv": (dkdv_flops(w), dkdv_bytes(w) + ds_tile_bytes(w)),
+                "dq": (dq_ds_flops(w), dq_ds_bytes(w))}
+    return {"dkdv": (dkdv_flops(w), dkdv_bytes(w)), "dq": (dq_flops(w), dq_bytes(w))}
+
+
+def resolved_mode(attn, w, torch_dtype) -> str:
+    """The dQ mode the library's ATTN_DQ_AUTO takes for a workload: read off
+    its workspace size, which is that of the mode it picks."""
+    def size(mode):
+        return attn.bwd_workspace_bytes(w.B, w.H, w.n, w.m, w.d, w.dv, torch_dtype,
+                                        dq_mode=mode, causal=w.causal)
+    auto = size("auto")
+    if auto == size("stored_ds") and auto != size("separate"):
+        return "stored_ds"
+    return "separate"
 
 
 def dkdv_bytes(w) -> float:
@@ -211,7 +252,7 @@ TABLE_WORKLOADS = ("causal_1k_d64", "causal_4k_d128", "causal_16k_d128",
                    "cross_512x2048_d128_dv64", "causal_4k_d128_fp16")
 
 
-def mode_figures(w, run, steps, torch, split=None):
+def mode_figures(w, run, steps, torch, split=None, mode="separate"):
     """Whole-backward and per-kernel timings of one dQ mode."""
     # the first launches after another workload's run come at a lower clock
     ms = time_loop(run, steps, torch, 8)
@@ -220,7 +261,8 @@ def mode_figures(w, run, steps, torch, split=None):
     k_dq = time_loop(lambda: run(["preprocess", "dq"]), steps, torch, 2)
     nkeys = (split or 0) * 256
     if split is None:
-        f_dkdv, f_dq = dkdv_flops(w), dq_flops(w)
+        kf = mode_kernels(w, mode)
+        f_dkdv, f_dq = kf["dkdv"][0], kf["dq"][0]
     else:
         # the fused kernel also forms dS K for the keys past the split; the
         # separate pass recomputes S and dP only for the keys before it
@@ -245,9 +287,9 @@ def mode_figures(w, run, steps, torch, split=None):
 
 
 def workload_table(names, steps, torch, attn, make_inputs, workloads):
-    """For each workload: the backward in the separate-pass dQ mode and in
-    the atomic mode at the best of a few splits (leading 256-key blocks left
-    to the separate pass)."""
+    """For each workload: the backward in the separate-pass and stored-dS dQ
+    modes, and in the atomic mode at the best of a few splits (leading
+    256-key blocks left to the separate pass)."""
     table = {}
     dev = "cuda:0"
     for name in names:
@@ -262,14 +304,16 @@ def workload_table(names, steps, torch, attn, make_inputs, workloads):
             key = mode
             if key not in wss:
                 wss[key] = torch.empty(max(attn.bwd_workspace_bytes(
-                    w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype, dq_mode=mode), 1),
+                    w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype, dq_mode=mode, causal=w.causal), 1),
                     dtype=torch.uint8, device=dev)
             return lambda stages=None: attn.bwd(
                 q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, dq_mode=mode,
                 dq_split=split, workspace=wss[key], dq=dq, dk=dk, dv=dv, stages=stages)
 
-        row = {"flops": bwd_flops(w),
-               "separate": mode_figures(w, runner("separate", None), steps, torch)}
+        row = {"flops": bwd_flops(w), "auto_mode": resolved_mode(attn, w, q.dtype),
+               "separate": mode_figures(w, runner("separate", None), steps, torch),
+               "stored_ds": mode_figures(w, runner("stored_ds", None), steps, torch,
+                                         mode="stored_ds")}
         nkb = (w.m + 255) // 256
         splits = sorted({0} | {max(1, (nkb * f) // 8) for f in (1, 2, 3, 4, 6)})
         tried = {sp: time_loop(runner("atomic", sp), max(3, steps // 2), torch, 2)
@@ -349,7 +393,10 @@ def main():
     inputs_cpu = make_inputs(w, "cpu")
     q, k, v, do = (t.to(dev) for t in inputs_cpu)
     o, lse = attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal)
-    ws = torch.empty(max(attn.bwd_workspace_bytes(w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype), 1),
+    # the library's own choice of dQ mode (ATTN_DQ_AUTO) is what is timed
+    mode = resolved_mode(attn, w, q.dtype)
+    ws = torch.empty(max(attn.bwd_workspace_bytes(w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype,
+                                                  causal=w.causal), 1),
                      dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
@@ -381,8 +428,8 @@ def main():
         "preprocess": time_loop(lambda: bwd_step(["preprocess"]), args.steps, torch, 3),
         "dkdv": time_loop(lambda: bwd_step(["dkdv"]), args.steps, torch, 3),
         "dq": time_loop(lambda: bwd_step(["dq"]), args.steps, torch, 3),
-        # what a whole 16-bit backward launches first: the dQ pass with the
-        # preprocess in its prologue
+        # the separate mode launches the dQ pass first with the preprocess in
+        # its prologue; the stored-dS mode launches the two on their own
         "dq_with_preprocess": time_loop(lambda: bwd_step(["preprocess", "dq"]), args.steps,
                                         torch, 3),
     }
@@ -395,8 +442,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     dk_tf = dkdv_flops(w) / (kern_ms["dkdv"] * 1e-3) / 1e12
     dominant = max(("dkdv", "dq"), key=lambda kname: kern_ms[kname])
-    dom_flops = dkdv_flops(w) if dominant == "dkdv" else dq_flops(w)
-    dom_bytes = dkdv_bytes(w) if dominant == "dkdv" else dq_bytes(w)
+    dom_flops, dom_bytes = mode_kernels(w, mode)[dominant]
     dom_tf = dom_flops / (kern_ms[dominant] * 1e-3) / 1e12
     mask = "causal" if w.causal else "non-causal"
     shape = f"N={w.n}" if w.n == w.m else f"n={w.n}, m={w.m}"
@@ -422,6 +468,7 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
+        "dq_mode": mode,
         "kernels_ms": {k_: round(v_, 4) for k_, v_ in kern_ms.items()},
         "fwd": {"ms": round(fwd_ms, 4),
                 "tflops": round(fwd_flops(w) / (fwd_ms * 1e-3) / 1e12, 2),

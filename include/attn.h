@@ -19,7 +19,8 @@
  *   dS = P o (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
  *
  * The backward recomputes P tile by tile from Q, K and LSE (mlgrind "Edge
- * cases and conventions"); it never stores an n x m matrix.
+ * cases and conventions"); it never stores P.  Only the stored-dS dQ mode
+ * (ATTN_DQ_STORED_DS below) keeps an n x m matrix, dS, in the workspace.
  *
  * Conventions for every entry point:
  *  - Tensors are device pointers to contiguous row-major [B, H, rows, cols]
@@ -108,14 +109,29 @@ enum attn_status {
  *                    associative, so dq can differ in its last bits from run
  *                    to run; dk and dv are deterministic in every mode.
  *                    16-bit dtypes only.
- *  ATTN_DQ_AUTO      the library's choice of mode and split for the shapes,
- *                    from measurements on MI355X.
+ *  ATTN_DQ_STORED_DS the dK/dV kernel also writes the dS it forms (rounded
+ *                    to the input type, as the products use it) into the
+ *                    workspace, and a third pass forms dQ = scale * dS K
+ *                    from it, recomputing nothing: deterministic, the
+ *                    matrix work of the formulas alone, at the price of 2
+ *                    bytes of workspace per (query, key) pair in visited
+ *                    256 x 256 tiles (under the causal mask only the tiles
+ *                    on and below the diagonal; see
+ *                    attn_bwd_workspace_bytes_ex).  16-bit dtypes; not with
+ *                    ATTN_MASK_CAUSAL_BOTTOM_RIGHT unless n == m and both
+ *                    length arrays are NULL; one head's tiles at most 2^31
+ *                    bytes.  Otherwise ATTN_EUNSUPPORTED.
+ *  ATTN_DQ_AUTO      the library's choice for the shapes, from measurements
+ *                    on MI355X: the separate pass, which was the fastest
+ *                    mode at every shape timed (writing and re-reading dS
+ *                    cost more than its recomputation there).
  */
 #define ATTN_DQ_SPLIT(k) ((int)(k) << 12) /* k in 0..255, with ATTN_DQ_ATOMIC only */
 enum attn_bwd_flags {
     ATTN_DQ_AUTO = 0,
     ATTN_DQ_ATOMIC = 1,
     ATTN_DQ_SEPARATE = 2,
+    ATTN_DQ_STORED_DS = 3,
     /* Bits 8-10 restrict which kernels run (0 = all).  They exist so that
        each kernel can be timed on its own; a caller wanting gradients
        leaves them 0.  Later stages read what earlier ones wrote (the
@@ -161,10 +177,24 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int layout, int dtype, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes and flags (a
- * multiple of 256; zero for an empty problem).  Holds per-row D and
- * rescaled LSE, and with ATTN_DQ_ATOMIC or ATTN_DQ_AUTO (16-bit dtypes) the
- * float32 dQ accumulator, B*H*round_up(n, 128)*(64 or 128) floats.
+ * Bytes of device workspace attn_bwd_ex needs for these sizes, mask mode
+ * (enum attn_mask) and flags (a multiple of 256; zero for an empty problem
+ * or invalid arguments).  Holds per-row D and rescaled LSE
+ * (2*B*H*round_up(n, 128) floats), plus, in the dQ mode the flags select
+ * (16-bit dtypes; ATTN_DQ_AUTO needs nothing more):
+ *  - ATTN_DQ_ATOMIC: the float32 dQ accumulator, B*H*round_up(n, 128)*(64
+ *    or 128) floats;
+ *  - ATTN_DQ_STORED_DS: B*H*t tiles of 256*256 16-bit dS values, with
+ *    t = N(N+1)/2 under a causal mask and t = N*M without one,
+ *    N = ceil(n/256), M = ceil(m/256).
+ */
+size_t attn_bwd_workspace_bytes_ex(int B, int H, int n, int m, int d, int dv, int mask,
+                                   int dtype, int flags);
+
+/*
+ * attn_bwd_workspace_bytes_ex without a mask argument: the size for
+ * ATTN_MASK_NONE, which is at least the size for either causal mode, so it
+ * suffices for attn_bwd and attn_bwd_ex with any mask.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags);
@@ -199,12 +229,12 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
  * attn_bwd_ex for callers that cannot allocate device memory (code under
  * stream capture, tight serving loops, harnesses that forbid allocation):
  * no workspace argument.  The per-row D and rescaled LSE (and, in the
- * atomic dQ mode, the float32 dQ accumulator) go to a static device array
- * of ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it
- * runs on until the process ends.  ATTN_DQ_AUTO is first resolved to the
- * mode the library picks; a problem whose scratch (attn_bwd_workspace_bytes
- * with that mode) exceeds the array returns ATTN_ESCRATCH before anything
- * is enqueued.  Every call on a GPU shares that GPU's one array and leaves
+ * atomic dQ mode, the float32 dQ accumulator; in the stored-dS mode the dS
+ * tiles) go to a static device array of ATTN_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on each GPU it runs on until the process ends.
+ * ATTN_DQ_AUTO runs the separate pass here; a problem whose scratch
+ * (attn_bwd_workspace_bytes_ex with that mode) exceeds the array returns
+ * ATTN_ESCRATCH before anything is enqueued.  Every call on a GPU shares that GPU's one array and leaves
  * its contents there: calls that overlap on one GPU (different streams or
  * host threads) race and give wrong results, so serialise them.  The first
  * call on each device looks up the array's address (hipGetSymbolAddress,

@@ -41,28 +41,51 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # separate dQ pass: two float32 arrays of B*H*round_up(n, 128) rows
-    # (rounded to 256 bytes); the atomic and automatic modes add the float32
-    # dQ accumulator, rows x (64 or 128, the tile width for d)
-    sep, atom = B.ATTN_DQ_SEPARATE, B.ATTN_DQ_ATOMIC
-    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="separate") == \
-        2 * 64 * 4096 * 4
-    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128) == 64 * 4096 * 4 * (2 + 128)
+    # separate dQ pass (also what the automatic mode runs): two float32
+    # arrays of B*H*round_up(n, 128) rows (rounded to 256 bytes); the atomic
+    # mode adds the float32 dQ accumulator, rows x (64 or 128, the tile
+    # width for d); the stored-dS mode adds 256 x 256 16-bit dS tiles:
+    # N(N+1)/2 per head under a causal mask, N*M without one (N, M query and
+    # key blocks of 256)
+    sep, atom, sds = B.ATTN_DQ_SEPARATE, B.ATTN_DQ_ATOMIC, B.ATTN_DQ_STORED_DS
+    tile = 256 * 256 * 2
+    rows4k = 2 * 64 * 4096 * 4
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="separate") == rows4k
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128) == rows4k
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, causal=True) == rows4k
     assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="atomic") == \
         64 * 4096 * 4 * (2 + 128)
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="stored_ds") == \
+        rows4k + 64 * 16 * 16 * tile
+    assert attn.bwd_workspace_bytes(2, 32, 4096, 4096, 128, 128, dq_mode="stored_ds",
+                                    causal=True) == rows4k + 64 * 136 * tile
+    assert attn.bwd_workspace_bytes(1, 32, 16384, 16384, 128, 128, dq_mode="stored_ds",
+                                    causal=True) == 2 * 32 * 16384 * 4 + 32 * 2080 * tile
     assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64, dq_mode="separate") == 2 * 128 * 4
-    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64) == 128 * 4 * (2 + 64)
+    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64) == 2 * 128 * 4
+    assert attn.bwd_workspace_bytes(1, 1, 1, 1, 64, 64, dq_mode="stored_ds") == 2 * 128 * 4 + tile
     assert attn.bwd_workspace_bytes(1, 1, 0, 5, 64, 64) == 0
     assert attn.bwd_workspace_bytes(0, 4, 100, 5, 64, 64) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 100, 100, B.ATTN_BF16, 0) == 0  # unsupported
     for code in (B.ATTN_BF16, B.ATTN_F16, B.ATTN_F32):
         assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, sep) == 2 * 6 * 384 * 4
+        assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, 0) == 2 * 6 * 384 * 4
     for code in (B.ATTN_BF16, B.ATTN_F16):
         assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, code, atom) == \
             6 * 384 * 4 * (2 + 64)
         assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 96, 64, code, atom) == \
             6 * 384 * 4 * (2 + 128)
-    # float32 has no fused dQ: no accumulator in any mode
+        # 300 queries, 700 keys: 2 query blocks, 3 key blocks
+        assert lib.attn_bwd_workspace_bytes_ex(2, 3, 300, 700, 64, 64, B.ATTN_MASK_NONE, code,
+                                               sds) == 2 * 6 * 384 * 4 + 6 * 6 * tile
+        assert lib.attn_bwd_workspace_bytes_ex(2, 3, 300, 700, 64, 64, B.ATTN_MASK_CAUSAL, code,
+                                               sds) == 2 * 6 * 384 * 4 + 6 * 3 * tile
+        assert lib.attn_bwd_workspace_bytes_ex(2, 3, 300, 300, 64, 64,
+                                               B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT, code, sds) == \
+            2 * 6 * 384 * 4 + 6 * 3 * tile
+    assert lib.attn_bwd_workspace_bytes_ex(1, 1, 8, 8, 64, 64, 3, B.ATTN_BF16, 0) == 0  # bad mask
+    # float32 has no fused dQ and no stored dS: nothing beyond the rows in
+    # the automatic mode
     assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, B.ATTN_F32, 0) == 2 * 6 * 384 * 4
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 64, 136, B.ATTN_F16, 0) == 0  # unsupported
     assert lib.attn_bwd_workspace_bytes(1, 1, 8, 8, 96, 40, B.ATTN_F16, 0) > 0
@@ -130,7 +153,16 @@ def test_workspace_checks(lib):
 def test_unknown_flags(lib):
     assert _bwd(lib, flags=1 << 20) == B.ATTN_EUNSUPPORTED
     assert _bwd(lib, flags=7) == B.ATTN_EUNSUPPORTED
-    assert _bwd(lib, flags=3) == B.ATTN_EUNSUPPORTED
+    assert _bwd(lib, flags=4) == B.ATTN_EUNSUPPORTED
+    assert _bwd(lib, flags=B.ATTN_DQ_STORED_DS | (1 << B.DQ_SPLIT_SHIFT)) == B.ATTN_EUNSUPPORTED
+    # the stored-dS mode: 16-bit types only, and no diagonal that moves
+    # with per-batch lengths
+    assert _bwd(lib, flags=B.ATTN_DQ_STORED_DS, dtype=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
+    lens = ctypes.c_void_p(1 << 20)
+    assert _bwd_ex(lib, flags=B.ATTN_DQ_STORED_DS, mask=B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT,
+                   sq=lens, sk=lens) == B.ATTN_EUNSUPPORTED
+    assert _bwd_ex(lib, flags=B.ATTN_DQ_STORED_DS, mask=B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT, n=64,
+                   m=128) == B.ATTN_EUNSUPPORTED
     # a split only with the atomic mode; the atomic mode only for 16-bit types
     assert _bwd(lib, flags=B.ATTN_DQ_SEPARATE | (1 << B.DQ_SPLIT_SHIFT)) == B.ATTN_EUNSUPPORTED
     assert _bwd(lib, flags=B.ATTN_DQ_AUTO | (2 << B.DQ_SPLIT_SHIFT)) == B.ATTN_EUNSUPPORTED
@@ -145,6 +177,7 @@ def test_dq_flag_constants_match_header():
     assert int(vals["ATTN_DQ_AUTO"]) == B.ATTN_DQ_AUTO == 0
     assert int(vals["ATTN_DQ_ATOMIC"]) == B.ATTN_DQ_ATOMIC == 1
     assert int(vals["ATTN_DQ_SEPARATE"]) == B.ATTN_DQ_SEPARATE == 2
+    assert int(vals["ATTN_DQ_STORED_DS"]) == B.ATTN_DQ_STORED_DS == 3
     m = re.search(r"#define ATTN_DQ_SPLIT\(k\) \(\(int\)\(k\) << (\d+)\)", text)
     assert m and int(m.group(1)) == B.DQ_SPLIT_SHIFT
 

@@ -1,13 +1,14 @@
-"""GPU parity of the two ways dQ is accumulated (ATTN_DQ_SEPARATE and
-ATTN_DQ_ATOMIC at several splits, and ATTN_DQ_AUTO) against the float64
-oracle, on seeded inputs spanning several 256-key blocks with ragged tails,
+"""GPU parity of the ways dQ is accumulated (ATTN_DQ_SEPARATE,
+ATTN_DQ_ATOMIC at several splits, ATTN_DQ_STORED_DS and ATTN_DQ_AUTO)
+against the float64 oracle, on seeded inputs spanning several 256-key blocks with ragged tails,
 every head-width pair, both 16-bit types, masks with per-batch lengths and
 the [B, seq, H, dim] layout.
 
-dK and dV do not depend on the dQ mode: the fused kernel's dK/dV arithmetic
-is the plain kernel's, so they must agree bit for bit across modes.  dQ in
-the atomic mode is summed in an order the hardware chooses, so it is held to
-the oracle's tolerance and to a tight agreement with the separate pass.
+dK and dV do not depend on the dQ mode: the fused and the dS-storing
+kernels' dK/dV arithmetic is the plain kernel's, so they must agree bit for
+bit across modes.  dQ in the atomic mode is summed in an order the hardware
+chooses, and in the stored-dS mode from the dK/dV kernel's dS, so it is held
+to the oracle's tolerance and to a tight agreement with the separate pass.
 """
 import numpy as np
 import pytest
@@ -42,7 +43,8 @@ SHAPES = [
 
 def _modes(w):
     nkb = (w.m + 255) // 256
-    modes = [("separate", None), ("auto", None), ("atomic", 0), ("atomic", 1)]
+    modes = [("separate", None), ("auto", None), ("stored_ds", None), ("atomic", 0),
+             ("atomic", 1)]
     if nkb > 2:
         modes.append(("atomic", nkb // 2))
     modes.append(("atomic", nkb))   # every key block in the separate pass
@@ -128,7 +130,10 @@ def test_dq_modes_masks_and_layouts(case):
     tol = TOL[dtype]
     nkb = (m + 255) // 256
     base = None
-    for mode, split in [("separate", None), ("atomic", 0), ("atomic", 1), ("atomic", nkb)]:
+    modes = [("separate", None), ("auto", None), ("atomic", 0), ("atomic", 1), ("atomic", nkb)]
+    if mask != "causal_bottom_right":
+        modes.append(("stored_ds", None))
+    for mode, split in modes:
         dq, dk, dvv = attn.bwd(qd, kd, vd, o, dod, lse, scale=scale, mask=mask, seqlens_q=sq,
                                seqlens_k=sk, layout=layout, dq_mode=mode, dq_split=split)
         torch.cuda.synchronize()
@@ -145,3 +150,40 @@ def test_dq_modes_masks_and_layouts(case):
             base = (dk.clone(), dvv.clone())
         else:
             assert torch.equal(dk, base[0]) and torch.equal(dvv, base[1]), (mode, split)
+
+
+def test_stored_ds_refuses_a_moving_diagonal():
+    """The stored-dS mode indexes dS tiles by a diagonal at j = i; with a
+    bottom-right diagonal and per-batch lengths it is refused before
+    anything runs, and ATTN_DQ_AUTO takes the separate pass there."""
+    say("case stored_ds refusal, bottom-right with lengths")
+    B, H, n, m, d = 2, 1, 200, 300, 64
+    g = torch.Generator().manual_seed(95)
+    q, k, v, do = (torch.randn(B, H, r, d, generator=g).to(torch.bfloat16).to("cuda:0")
+                   for r in (n, m, m, n))
+    sq = torch.tensor([200, 150], dtype=torch.int32, device="cuda:0")
+    sk = torch.tensor([300, 250], dtype=torch.int32, device="cuda:0")
+    o, lse = attn.fwd(q, k, v, mask="causal_bottom_right", seqlens_q=sq, seqlens_k=sk)
+    with pytest.raises(attn.AttnError) as e:
+        attn.bwd(q, k, v, o, do, lse, mask="causal_bottom_right", seqlens_q=sq,
+                 seqlens_k=sk, dq_mode="stored_ds")
+    assert e.value.status == attn.binding.ATTN_EUNSUPPORTED
+    a = attn.bwd(q, k, v, o, do, lse, mask="causal_bottom_right", seqlens_q=sq, seqlens_k=sk)
+    b = attn.bwd(q, k, v, o, do, lse, mask="causal_bottom_right", seqlens_q=sq, seqlens_k=sk,
+                 dq_mode="separate")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_stored_ds_is_deterministic():
+    """Two stored-dS calls give the same bits (no atomics in the mode)."""
+    w = SHAPES[0]
+    say(f"case stored_ds repeat {w.describe()}")
+    q, k, v, do = (t.to("cuda:0") for t in make_inputs(w))
+    o, lse = attn.fwd(q, k, v, scale=w.softmax_scale, causal=True)
+    a = attn.bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=True, dq_mode="stored_ds")
+    b = attn.bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=True, dq_mode="stored_ds")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -6,9 +6,9 @@ taken over the whole tensor.
 Every head of the 1k/d64, 4k/d128 (bf16 and fp16) and 512x2048 cross
 workloads is compared; the 16k/d128 workload is compared on two whole heads
 (the oracle needs about 4 s per head of it on 16 cores) and by sampled rows
-elsewhere.  The backward runs in both dQ modes on the same forward: the
-separate pass (what ATTN_DQ_AUTO picks) and the atomic mode at a middle
-split.
+elsewhere.  The backward runs in every dQ mode on the same forward: the
+separate pass (what ATTN_DQ_AUTO picks), the atomic mode at a middle split
+and the stored-dS mode.
 """
 import numpy as np
 import pytest
@@ -38,7 +38,7 @@ def _forward_backward(w, inputs, modes):
 
 def _modes(w):
     nkb = (w.m + 255) // 256
-    return [("separate", None), ("atomic", nkb // 2)]
+    return [("separate", None), ("atomic", nkb // 2), ("stored_ds", None)]
 
 
 def _check(w, got_o, got_lse, grads, ref, label):

@@ -22,7 +22,7 @@ _DTYPE_CODES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float1
 (ATTN_OK, ATTN_EINVAL, ATTN_ECAUSAL_SHAPE, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP,
  ATTN_ESCRATCH) = range(7)
 NOALLOC_SCRATCH_BYTES = 16 << 20
-ATTN_DQ_AUTO, ATTN_DQ_ATOMIC, ATTN_DQ_SEPARATE = 0, 1, 2
+ATTN_DQ_AUTO, ATTN_DQ_ATOMIC, ATTN_DQ_SEPARATE, ATTN_DQ_STORED_DS = 0, 1, 2, 3
 DQ_SPLIT_SHIFT, DQ_SPLIT_MAX = 12, 255
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
@@ -30,11 +30,12 @@ MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL,
 ATTN_LAYOUT_BHSD, ATTN_LAYOUT_BSHD = 0, 1
 LAYOUTS = {"bhsd": ATTN_LAYOUT_BHSD, "bshd": ATTN_LAYOUT_BSHD}
 ATTN_STAGE_PREPROCESS, ATTN_STAGE_DKDV, ATTN_STAGE_DQ = 1 << 8, 1 << 9, 1 << 10
-DQ_MODES = {"auto": ATTN_DQ_AUTO, "atomic": ATTN_DQ_ATOMIC, "separate": ATTN_DQ_SEPARATE}
+DQ_MODES = {"auto": ATTN_DQ_AUTO, "atomic": ATTN_DQ_ATOMIC, "separate": ATTN_DQ_SEPARATE,
+            "stored_ds": ATTN_DQ_STORED_DS}
 STAGES = {"preprocess": ATTN_STAGE_PREPROCESS, "dkdv": ATTN_STAGE_DKDV, "dq": ATTN_STAGE_DQ}
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
-            "attn_bwd_ex_noalloc",
+            "attn_bwd_workspace_bytes_ex", "attn_bwd_ex_noalloc",
             "attn_out_proj_bwd", "attn_in_proj_bwd", "attn_status_str", "attn_version")
 
 _lib = None
@@ -60,6 +61,8 @@ def load():
     lib.attn_fwd.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
+    lib.attn_bwd_workspace_bytes_ex.argtypes = [I] * 9
+    lib.attn_bwd_workspace_bytes_ex.restype = Z
     lib.attn_bwd.argtypes = [vp] * 9 + [I] * 6 + [F, I, I, I, vp, Z, vp]
     lib.attn_bwd.restype = I
     lib.attn_fwd_ex.argtypes = [vp] * 7 + [I] * 6 + [F, I, I, I, vp]
@@ -221,11 +224,15 @@ def _dq_flags(dq_mode, dq_split):
     return flags
 
 
-def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto"):
+def bwd_workspace_bytes(B, H, n, m, d, dv, dtype=torch.bfloat16, dq_mode="auto", causal=False,
+                        mask=None):
+    """attn_bwd_workspace_bytes_ex: workspace bytes of a backward with these
+    sizes, mask (as in fwd()) and dQ mode."""
     code = _DTYPE_CODES.get(dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {dtype}; use bfloat16, float16 or float32")
-    return int(load().attn_bwd_workspace_bytes(B, H, n, m, d, dv, code, _dq_flags(dq_mode, None)))
+    return int(load().attn_bwd_workspace_bytes_ex(B, H, n, m, d, dv, _mask_code(causal, mask),
+                                                  code, _dq_flags(dq_mode, None)))
 
 
 def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, layout, dq_mode, dq_split, stages, scale):
@@ -264,7 +271,7 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
         layout="bhsd", dq_split=None):
     """(dq, dk, dv) with the shapes and dtype of (q, k, v).
 
-    ``dq_mode`` is "auto", "separate" or "atomic" (ATTN_DQ_*), and
+    ``dq_mode`` is "auto", "separate", "atomic" or "stored_ds" (ATTN_DQ_*), and
     ``dq_split`` the number of leading 256-key blocks whose dQ the separate
     pass sums in the atomic mode.  ``stages`` (a subset of {"preprocess",
     "dkdv", "dq"}) restricts which kernels run; it exists for timing single
@@ -276,7 +283,8 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, dq_mode="auto", workspace
         raise TypeError(f"workspace must be torch.uint8, got {workspace.dtype}")
     (B, H, n, m, d, dvw), code, flags, scale = _bwd_args(
         q, k, v, o, do, lse, dq, dk, dv, layout, dq_mode, dq_split, stages, scale)
-    need = int(lib.attn_bwd_workspace_bytes(B, H, n, m, d, dvw, code, flags))
+    need = int(lib.attn_bwd_workspace_bytes_ex(B, H, n, m, d, dvw, _mask_code(causal, mask),
+                                               code, flags))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_dev(workspace)

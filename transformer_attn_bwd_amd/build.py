@@ -27,7 +27,8 @@ OBJ_DIR = os.path.join(ROOT, "_build")
 # 16-bit element type, so that the slow instantiations build in parallel.
 ELEMS = ("bf16", "f16")
 MFMA_SOURCES = ["attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dkdv_dqa.hip",
-                "attn_bwd_dq_mfma.hip", "attn_proj_gemm.hip"]
+                "attn_bwd_dkdv_dss.hip", "attn_bwd_dq_mfma.hip", "attn_bwd_dq_ds.hip",
+                "attn_proj_gemm.hip"]
 SOURCES = ["attn_api.hip", "attn_f32.hip", *MFMA_SOURCES]
 UNITS = [("attn_api.hip", None), ("attn_f32.hip", None)] + [
     (src, elem) for src in MFMA_SOURCES for elem in ELEMS]

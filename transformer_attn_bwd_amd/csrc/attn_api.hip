@@ -99,29 +99,60 @@ bool tensor_ok(const void* p, long elems, int dtype) {
 // width for d.
 int acc_width(const Problem& p) { return (attn::mfma_widths(p) >> 8) == 0x40 ? 64 : 128; }
 
-// Whether the flags' dQ mode can need the accumulator (ATTN_DQ_AUTO may pick
-// the atomic mode, so it reserves the space too).
-bool may_use_acc(const Problem& p, int flags) {
+// Whether the stored dS tiles of a problem are indexed triangularly.
+bool ds_tri(const Problem& p) { return p.causal; }
+
+// Bytes of one head's stored dS tiles (16-bit, 256 x 256 each).
+size_t ds_head_bytes(const Problem& p) {
+    return (size_t)attn::ds_tiles_per_head(p.n, p.m, ds_tri(p)) * attn::kDsTile * attn::kDsTile *
+           2;
+}
+constexpr size_t kMaxDsHeadBytes = (size_t)1 << 31;
+
+// Stored-dS mode: dS tiles are indexed triangularly when the causal
+// diagonal is j = i in every batch element (top-left, or bottom-right
+// with n == m and no per-batch lengths), densely without a mask; a
+// bottom-right diagonal that can move per batch element is not supported.
+bool ds_supported(const Problem& p) {
+    if (!is_16bit(p.dtype) || attn::mfma_widths(p) == 0) return false;
+    if (p.mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT &&
+        (p.n != p.m || p.seqlens_q != nullptr || p.seqlens_k != nullptr))
+        return false;
+    // one head's tiles are addressed with 32-bit byte offsets
+    return ds_head_bytes(p) <= kMaxDsHeadBytes;
+}
+
+size_t ds_bytes(const Problem& p) {
+    return round_up((size_t)p.heads() * ds_head_bytes(p), 256);
+}
+
+// The concrete dQ mode of a call: ATTN_DQ_SEPARATE, ATTN_DQ_ATOMIC or
+// ATTN_DQ_STORED_DS (float32 always runs the separate pass).  ATTN_DQ_AUTO
+// is the separate pass: on MI355X it measured fastest at every workload
+// shape timed (causal n = 1k to 16k at d = 64 and 128, cross 512 x 2048),
+// ahead of the atomic mode at its best split and of the stored-dS mode.
+int resolve_mode(const Problem& p, int flags) {
     const int mode = flags & kDqModeMask;
-    return is_16bit(p.dtype) && (mode == ATTN_DQ_ATOMIC || mode == ATTN_DQ_AUTO);
+    if (!is_16bit(p.dtype)) return ATTN_DQ_SEPARATE;
+    return mode == ATTN_DQ_AUTO ? ATTN_DQ_SEPARATE : mode;
 }
 
 size_t workspace_bytes(const Problem& p, int flags) {
     if (p.heads() == 0 || p.n == 0) return 0;
     const size_t rows = (size_t)p.heads() * (size_t)attn::padded_rows(p.n);
     size_t bytes = round_up(2 * rows * sizeof(float), 256);
-    if (may_use_acc(p, flags)) bytes += round_up(rows * acc_width(p) * sizeof(float), 256);
+    const int mode = resolve_mode(p, flags);
+    if (mode == ATTN_DQ_ATOMIC) bytes += round_up(rows * acc_width(p) * sizeof(float), 256);
+    if (mode == ATTN_DQ_STORED_DS) bytes += ds_bytes(p);
     return bytes;
 }
 
-// How dQ is accumulated for a 16-bit backward: -1 for the separate pass,
-// else the number of leading 256-key blocks the separate pass sums before
-// the fused dK/dV kernel adds the rest with atomics.
+// How dQ is accumulated for a 16-bit backward in the atomic mode: the
+// number of leading 256-key blocks the separate pass sums before the fused
+// dK/dV kernel adds the rest with atomics; -1 in the other modes.
 int resolve_dq(const Problem& p, int flags) {
-    const int mode = flags & kDqModeMask;
-    if (!is_16bit(p.dtype) || mode == ATTN_DQ_SEPARATE) return -1;
-    if (mode == ATTN_DQ_ATOMIC) return (flags & kSplitMask) >> kSplitShift;
-    return -1;   // ATTN_DQ_AUTO
+    if (resolve_mode(p, flags) != ATTN_DQ_ATOMIC) return -1;
+    return (flags & kSplitMask) >> kSplitShift;
 }
 
 constexpr int kMaxDevices = 64;
@@ -200,6 +231,38 @@ int bwd_atomic(const Problem& p, const void* q, const void* k, const void* v, co
                ? bwd_atomic_t<__bf16>(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, split, stages, s)
                : bwd_atomic_t<_Float16>(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, split, stages,
                                         s);
+}
+
+// The 16-bit backward in the stored-dS mode: the preprocess, the dK/dV
+// kernel that also writes dS to the workspace's tiles, and dQ = scale dS K
+// from those tiles.
+template <typename T>
+int bwd_stored_t(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv_out,
+                 const attn::Workspace& w, int stages, hipStream_t s) {
+    int st;
+    if (p.n > 0 && (stages & ATTN_STAGE_PREPROCESS)) {
+        if (!attn::launch_bwd_preprocess_mfma<T>(p, o, dout, lse, w, s)) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (stages & ATTN_STAGE_DKDV) {
+        if (!attn::launch_bwd_dkdv_dss_mfma<T>(p, q, k, v, dout, w, dk, dv_out, s))
+            return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    if (p.n > 0 && (stages & ATTN_STAGE_DQ)) {
+        if (!attn::launch_bwd_dq_ds_mfma<T>(p, k, w, dq, s)) return ATTN_EUNSUPPORTED;
+        if ((st = hip_status()) != ATTN_OK) return st;
+    }
+    return ATTN_OK;
+}
+
+int bwd_stored(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv_out,
+               const attn::Workspace& w, int stages, hipStream_t s) {
+    return p.dtype == ATTN_BF16
+               ? bwd_stored_t<__bf16>(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, stages, s)
+               : bwd_stored_t<_Float16>(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, stages, s);
 }
 
 // Sizes of the projection calls: T >= 0, widths multiples of 8 (16-byte
@@ -283,11 +346,17 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                        stream);
 }
 
+size_t attn_bwd_workspace_bytes_ex(int B, int H, int n, int m, int d, int dv, int mask,
+                                   int dtype, int flags) {
+    Problem p;
+    if (check_problem(B, H, n, m, d, dv, 1.f, mask, dtype, &p) != ATTN_OK) return 0;
+    return workspace_bytes(p, flags);
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags) {
-    Problem p;
-    if (check_problem(B, H, n, m, d, dv, 1.f, 0, dtype, &p) != ATTN_OK) return 0;
-    return workspace_bytes(p, flags);
+    // without the mask: the larger (unmasked, dense) stored-dS layout
+    return attn_bwd_workspace_bytes_ex(B, H, n, m, d, dv, ATTN_MASK_NONE, dtype, flags);
 }
 
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -304,10 +373,12 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     p.seqlens_k = seqlens_k;
     if (flags & ~(kDqModeMask | kStageMask | kSplitMask)) return ATTN_EUNSUPPORTED;
     const int dq_mode = flags & kDqModeMask;
-    if (dq_mode != ATTN_DQ_AUTO && dq_mode != ATTN_DQ_SEPARATE && dq_mode != ATTN_DQ_ATOMIC)
+    if (dq_mode != ATTN_DQ_AUTO && dq_mode != ATTN_DQ_SEPARATE && dq_mode != ATTN_DQ_ATOMIC &&
+        dq_mode != ATTN_DQ_STORED_DS)
         return ATTN_EUNSUPPORTED;
     if ((flags & kSplitMask) && dq_mode != ATTN_DQ_ATOMIC) return ATTN_EUNSUPPORTED;
     if (dq_mode == ATTN_DQ_ATOMIC && !is_16bit(dtype)) return ATTN_EUNSUPPORTED;
+    if (dq_mode == ATTN_DQ_STORED_DS && !ds_supported(p)) return ATTN_EUNSUPPORTED;
     const long hq = p.heads() * (long)n, hk = p.heads() * (long)m;
     if (!tensor_ok(q, hq * d, dtype) || !tensor_ok(k, hk * d, dtype) ||
         !tensor_ok(v, hk * dv, dtype) || !tensor_ok(o, hq * dv, dtype) ||
@@ -332,6 +403,14 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
     (void)hipGetLastError();
 
     const bool bf = is_16bit(dtype);
+    if (resolve_mode(p, flags) == ATTN_DQ_STORED_DS) {
+        const size_t head = ds_head_bytes(p);
+        w.ds.p = (char*)workspace + round_up(2 * (size_t)p.heads() * w.n_pad * 4, 256);
+        w.ds.head_elems = (long)(head / 2);
+        w.ds.tri = ds_tri(p) ? 1 : 0;
+        w.ds.mblk = (m + attn::kDsTile - 1) / attn::kDsTile;
+        return bwd_stored(p, q, k, v, o, dout, lse, dq, dk, dv_out, w, stages, s);
+    }
     const int split = resolve_dq(p, flags);
     if (split >= 0) {
         w.dqacc = (float*)((char*)workspace + round_up(2 * (size_t)p.heads() * w.n_pad * 4, 256));
@@ -394,12 +473,13 @@ int attn_bwd_ex_noalloc(const void* q, const void* k, const void* v, const void*
     int st = check_problem(B, H, n, m, d, dv, scale, mask, dtype, &p);
     if (st != ATTN_OK) return st;
     if (flags & ~(kDqModeMask | kStageMask | kSplitMask)) return ATTN_EUNSUPPORTED;
-    // ATTN_DQ_AUTO becomes the mode it resolves to, so that the size check
-    // counts the accumulator only when the atomic mode really runs.
+    p.seqlens_q = seqlens_q;
+    p.seqlens_k = seqlens_k;
+    // ATTN_DQ_AUTO becomes the mode it resolves to (the separate pass), so
+    // that the size check below is that of the mode that runs.
     if ((flags & kDqModeMask) == ATTN_DQ_AUTO) {
-        const int split = resolve_dq(p, flags);
         flags &= ~(kDqModeMask | kSplitMask);
-        flags |= split < 0 ? ATTN_DQ_SEPARATE : (ATTN_DQ_ATOMIC | ATTN_DQ_SPLIT(split));
+        flags |= ATTN_DQ_SEPARATE;
     }
     const size_t need = workspace_bytes(p, flags);
     if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ESCRATCH;

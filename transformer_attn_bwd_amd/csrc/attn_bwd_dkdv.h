@@ -109,6 +109,11 @@ struct DkdvSched {
 // every bank once.
 constexpr int kDsCols = 32;
 
+// dS stores per wave and step in the stored-dS kernel: four 8-value packs,
+// each as two 8-byte stores; also the vmcnt field of the step's closing
+// s_waitcnt (expcnt and lgkmcnt fields zero).
+constexpr int kDssStores = 8;
+
 // The lane index, computed where it is needed: the asm cannot be moved out
 // of a loop, so no register holds the index (or values derived from it)
 // through one.
@@ -131,18 +136,19 @@ __device__ __forceinline__ int ds_tile_off(int r, int cgrp) {
 // layout, so swapping them yields the transposed product in the same
 // registers, and the transposed tiles hold four consecutive columns of one
 // key per lane group, which the epilogue needs.
-template <typename T, int D, int DV, bool CAUSAL, bool DQA>
+template <typename T, int D, int DV, bool CAUSAL, bool DQA, bool DSS>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ Dw, T* __restrict__ dk, T* __restrict__ dvo,
     float* __restrict__ dqacc, int dqa_from, int n, int m, int dg, int dvg, int n_pad,
-    float scale, float c2, SeqInfo si) {
+    float scale, float c2, SeqInfo si, DsTiles dst) {
     using C = DkdvCfg<D, DV>;
     using SC = DkdvSched<D, DV>;
     // the 128/128 kernel without the fused dQ forms P and dS slots before
     // the products that read them (checked in the assembly at build time)
     constexpr bool kOperandWait = DQA || D != 128 || DV != 128;
+    static_assert(!(DQA && DSS), "one dQ mode per instantiation");
     constexpr int BM = C::BM, NW = C::NW, LA = C::LA;
     // One LDS variable per buffer: the compiler can then tell that reads
     // of one buffer do not alias the asynchronous fills of the other, and
@@ -279,6 +285,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // instead of being kept through the loop.
     const bool dqa_on = DQA && j0 >= dqa_from;
     const bool ragged = j0 + C::BN > mb;
+    // Stored dS (DSS): this head's tiles, and this wave's 64 key rows of
+    // them (32768 bytes per 64 rows of 256 queries).
+    const __amdgpu_buffer_rsrc_t rds =
+        make_rsrc(DSS ? reinterpret_cast<const T*>(dst.p) + bh * dst.head_elems : q,
+                  DSS ? (uint32_t)(dst.head_elems * 2) : 0u);
+    const int kblk = to.rank;
     constexpr int NXQ = D / 32, WPB = NW / NXQ;
     const int xq = wave % NXQ, kq0 = (wave / NXQ) * (C::BN / WPB);
     auto opaque_lane = []() __attribute__((always_inline)) { return lane_id_here(); };
@@ -434,6 +446,28 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             *reinterpret_cast<vec4<T>*>(b + ds_tile_off(r, 4 * c + 2 + gg)) = vec4<T>{w[4], w[5], w[6], w[7]};
         };
 
+        // Stored dS: pack (kt, c) of this lane's key goes to key row
+        // 64 wave + 32 kt + (lane & 31) of the step's [256 keys][32 queries]
+        // block of tile (i0 / 256, kblk), columns 16c + 4g .. +3 and
+        // 16c + 8 + 4g .. +3 (two 8-byte stores).  The block is contiguous,
+        // so the four stores of a key tile fill whole 128-byte lines
+        // together.
+        auto ds_gstore = [&](auto p_) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_)::value, kt = p % 2, c = p / 2;
+            const int l = opaque_lane();
+            vec8<T> w = dSb[kt][c];
+            if (ragged) w = kw0 + 32 * kt + (l & 31) < mb ? w : vec8<T>{};
+            const u32x4 bits = __builtin_bit_cast(u32x4, w);
+            const int b = i0 / kDsTile;
+            const long tile = dst.tri ? (long)b * (b + 1) / 2 + kblk : (long)b * dst.mblk + kblk;
+            const uint32_t so =
+                (uint32_t)((tile * kDsTile * kDsTile + (i0 % kDsTile) * kDsTile) * 2) +
+                (uint32_t)(64 * BM * 2 * wave);
+            const uint32_t vo = (uint32_t)((l & 31) * (BM * 2) + (l >> 5) * 8 + 32 * c +
+                                           32 * BM * 2 * kt);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{bits[0], bits[1]}, rds, vo, so, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{bits[2], bits[3]}, rds, vo + 16, so, 0);
+        };
 
         // Fused dQ first: the previous step's product, before this step's
         // products, while the softmax values of the step are not yet live.
@@ -510,6 +544,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                         if (dqa_on) ds_store(std::integral_constant<int, t>{});
                     }
                 }
+                if constexpr (DSS) {
+                    constexpr int t = j - SC::J_DK;
+                    if constexpr (t < 4) ds_gstore(std::integral_constant<int, t>{});
+                }
             }
             // softmax work of this slot
             static_for<32>([&](auto i_) {
@@ -539,7 +577,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if (dqa_on && s >= 2) dq_atomics_parked(i0 - 2 * BM);
             }
             compute(buf_, masked_, i0);
-            __builtin_amdgcn_s_waitcnt(0);
+            if constexpr (DSS) {
+                // The next tile's loads were issued before this step's eight
+                // dS stores, and vector memory operations count down in the
+                // order they were issued: waiting until at most eight
+                // remain waits for the loads and leaves the stores in
+                // flight (lgkmcnt(0): this step's LDS accesses are done).
+                __builtin_amdgcn_s_waitcnt(kDssStores);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
             __syncthreads();
         };
 
@@ -679,7 +726,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 }
 
-template <typename T, int D, int DV, bool DQA>
+template <typename T, int D, int DV, bool DQA, bool DSS = false>
 void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
                  const void* dout, const Workspace& w, void* dk, void* dv, float* dqacc,
                  int dqa_from, hipStream_t s) {
@@ -688,13 +735,15 @@ void launch_dkdv(const Problem& p, const void* q, const void* k, const void* v,
     const float c2 = p.scale * kLog2e;
     const SeqInfo si = seq_info(p);
     if (p.causal)
-        bwd_dkdv_kernel<T, D, DV, true, DQA><<<grid, 256, 0, s>>>(
+        bwd_dkdv_kernel<T, D, DV, true, DQA, DSS><<<grid, 256, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dk, (T*)dv, dqacc, dqa_from, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+            (T*)dk, (T*)dv, dqacc, dqa_from, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si,
+            w.ds);
     else
-        bwd_dkdv_kernel<T, D, DV, false, DQA><<<grid, 256, 0, s>>>(
+        bwd_dkdv_kernel<T, D, DV, false, DQA, DSS><<<grid, 256, 0, s>>>(
             (const T*)q, (const T*)k, (const T*)v, (const T*)dout, w.lse2, w.D,
-            (T*)dk, (T*)dv, dqacc, dqa_from, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si);
+            (T*)dk, (T*)dv, dqacc, dqa_from, p.n, p.m, p.d, p.dv, w.n_pad, p.scale, c2, si,
+            w.ds);
 }
 
 }  // namespace

@@ -100,6 +100,25 @@ __device__ __forceinline__ SeqLens seq_lens(const SeqInfo& si, long bh, int n, i
 constexpr int kRowPad = 128;
 inline int padded_rows(int n) { return (n + kRowPad - 1) / kRowPad * kRowPad; }
 
+// dS of the stored-dS dQ mode: 16-bit tiles of 256 queries x 256 keys, one
+// per query block b and key block r that the dK/dV kernel visits, each as
+// eight [256 keys][32 queries] row-major blocks (one per 32-query step of
+// the dK/dV kernel, 16 KB contiguous): element (key j, query i) of a tile
+// at (i / 32) * 8192 + j * 32 + i % 32.  Tile (b, r) of a head sits at
+// index b (b + 1) / 2 + r when `tri` (causal with the diagonal at j = i:
+// the kernel visits r <= b only), else b * mblk + r.
+constexpr int kDsTile = 256;
+struct DsTiles {
+    void* p = nullptr;       // heads * head_elems elements of the input type
+    long head_elems = 0;     // elements per head (tiles * 256 * 256)
+    int tri = 0;
+    int mblk = 0;            // key blocks per query block (dense index)
+};
+inline long ds_tiles_per_head(int n, int m, bool tri) {
+    const long nb = (n + kDsTile - 1) / kDsTile, mb = (m + kDsTile - 1) / kDsTile;
+    return tri ? nb * (nb + 1) / 2 : nb * mb;
+}
+
 // Workspace view: lse2 [B*H][n_pad] then D [B*H][n_pad], float32; with the
 // fused dQ also the float32 dQ accumulator dqacc [B*H][n_pad][acc_w], acc_w
 // the 16-bit kernels' tile width for d (64 or 128).
@@ -109,6 +128,7 @@ struct Workspace {
     int n_pad;
     float* dqacc = nullptr;
     int acc_w = 0;
+    DsTiles ds;
 };
 
 // 16-bit MFMA path, T = __bf16 or _Float16 (instantiated in the kernel
@@ -138,6 +158,15 @@ template <typename T>
 bool launch_bwd_dkdv_dqa_mfma(const Problem& p, const void* q, const void* k, const void* v,
                               const void* dout, const Workspace& w, void* dk, void* dv,
                               float* dqacc, int dqa_from, hipStream_t s);
+// The dK/dV kernel that also writes its dS tiles to w.ds.
+template <typename T>
+bool launch_bwd_dkdv_dss_mfma(const Problem& p, const void* q, const void* k, const void* v,
+                              const void* dout, const Workspace& w, void* dk, void* dv,
+                              hipStream_t s);
+// dq = scale * dS K from the stored tiles of w.ds.
+template <typename T>
+bool launch_bwd_dq_ds_mfma(const Problem& p, const void* k, const Workspace& w, void* dq,
+                           hipStream_t s);
 // dq = scale * w.dqacc in T.
 template <typename T>
 void launch_dq_convert(const Problem& p, const Workspace& w, void* dq, hipStream_t s);
