@@ -41,8 +41,8 @@ KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip"
                   "attn_launch.h", "attn_bwd_dkdv_dss.hip", "attn_bwd_dq_ds.hip")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "c2def514fbd27039f477b308b003ce60067159eaae88fb23018064a96f0df8e0",
-    "bytes": {"bwd_dkdv": 7.6574e+08},
+    "sources_sha256": "c978122f653f4dc21562c6d67e8115c631aa3420725bc194b661c724d15a0590",
+    "bytes": {"bwd_dkdv": 7.6447e+08},
 }
 
 
