@@ -38,6 +38,11 @@ SHAPES = [
     _w("f16_cross_200x600_d128_dv64", 1, 1, 200, 600, 128, 64, "fp16", False, 88, 3.0),
     _w("bf16_single_key_block", 1, 1, 77, 200, 128, 128, "bf16", False, 89),
     _w("bf16_many_heads_causal_520", 4, 16, 520, 520, 128, 128, "bf16", True, 90),
+    # degenerate sizes: one query and one key, one ragged 32-row tile on the
+    # diagonal, one key for many rows
+    _w("bf16_one_query_one_key", 1, 1, 1, 1, 64, 64, "bf16", False, 96),
+    _w("bf16_causal_33_d128", 1, 2, 33, 33, 128, 128, "bf16", True, 97),
+    _w("bf16_257_queries_one_key", 1, 1, 257, 1, 128, 128, "bf16", False, 98),
 ]
 
 

@@ -2,8 +2,9 @@
 scratch is a static per-GPU array in the library), against attn_bwd_ex with
 a workspace on the same inputs.
 
-In the separate-pass dQ mode (what ATTN_DQ_AUTO picks) both entry points run
-the same kernels on the same data, so the outputs must agree bit for bit.
+In the separate-pass dQ mode (what ATTN_DQ_AUTO picks) and the stored-dS
+mode both entry points run the same kernels on the same data, so the
+outputs must agree bit for bit.
 In the atomic mode dQ is summed in an order the hardware chooses; there dK
 and dV must still agree bit for bit and dQ within the bf16 bar
 (max|err| / max|ref| <= 2e-2).  Each check makes two calls in a row, the
@@ -121,3 +122,19 @@ def test_noalloc_atomic_mode_two_calls():
         e = rel_err(to64(got[0]), to64(ref[0]))
         say(f"  dq vs workspace entry point {e:.3e}")
         assert e <= TOL["bf16"], (w.name, e)
+
+
+@pytest.mark.gpu
+def test_noalloc_stored_ds_two_calls():
+    """The stored-dS mode keeps its dS tiles in the static scratch (1.5 MB
+    and 0.4 MB here); deterministic, so bit for bit."""
+    cases = [
+        (_w("noalloc_stored_causal_600_d128", 1, 2, 600, 600, 128, 128, "bf16", True, 67), None),
+        (_w("noalloc_stored_cross_200x500_d64", 1, 2, 200, 500, 64, 64, "bf16", False, 68), None),
+    ]
+    for w, split in cases:
+        say(f"case noalloc stored_ds {w.describe()}")
+        ref, got = _pair(w, "stored_ds", split)
+        for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+            assert _same_bits(a, b), (w.name, name, rel_err(to64(b), to64(a)))
+    say("  bitwise equal on both calls")
