@@ -8,6 +8,12 @@ forward kernel, which runs before the timed region and is timed on its own
 as context.  FLOPs follow the convention 2nm(3d + 2dv) per head (10nmd when
 d = dv), halved for causal.
 
+Before the W warmup steps, untimed backward steps run for SETTLE_S seconds
+so that the GPU clock has settled under sustained load (it ramps for tens of
+milliseconds after idle); the JSON line's "settle" field reports them.
+Single-step durations come from HIP events without the system-scope fence
+(a default event writes back and invalidates the caches between steps).
+
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (N must be 1)
 --workload NAME --no-cpu-baseline --cpu-heads H --no-proj.
 
@@ -31,6 +37,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
+SETTLE_S = 0.25             # seconds of back-to-back backward steps before any timing
 
 # HBM bytes per launch of the dK/dV kernel (the dominant one) on causal_4k_d128, from
 # rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the
@@ -190,17 +197,77 @@ def time_loop(fn, steps, torch, warmup=0):
     return start.elapsed_time(end) / steps
 
 
+class _FenceFreeEvents:
+    """HIP timing events created with hipEventDisableSystemFence, recorded on
+    torch's current stream (the one the library launches on).  A default
+    event ends in a system-scope release: a writeback and invalidation of
+    the caches, which slows the step after it, so events between single
+    steps would time a step that no back-to-back loop runs.  These events
+    only timestamp; elapsed times are read after a device synchronisation."""
+    FLAG = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
+
+    def __init__(self, torch):
+        import ctypes
+        # the HIP runtime torch already loaded (one copy per process)
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        self.ct = ctypes
+        self.torch = torch
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.FLAG) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev
+
+    def record(self, ev):
+        stream = self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
 def step_times(fn, steps, torch):
-    """Per-step durations (ms) from an event pair around each step."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    """Per-step durations (ms) from a fence-free event pair around each of
+    `steps` back-to-back steps, sorted."""
+    ev = _FenceFreeEvents(torch)
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
     torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
+    for a, b in pairs:
+        ev.record(a)
         fn()
-        b.record()
+        ev.record(b)
     torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in evs)
+    out = sorted(ev.elapsed_ms(a, b) for a, b in pairs)
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    return out
+
+
+def settle(fn, torch, seconds):
+    """Run fn back to back until the GPU has been busy for `seconds` and
+    return (steps, seconds).  Under a sustained load the MI355X clock ramps
+    for the first few tens of milliseconds (4k backward in groups of ten
+    steps from idle: 1.14, 0.92, 0.88, 0.86, then 0.85 ms per step), so a
+    throughput taken right after idle times the ramp, not the kernels."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return n, dt
 
 
 def proj_flops(T, dm, hd, hdv) -> float:
@@ -255,7 +322,8 @@ TABLE_WORKLOADS = ("causal_1k_d64", "causal_4k_d128", "causal_16k_d128",
 def mode_figures(w, run, steps, torch, split=None, mode="separate"):
     """Whole-backward and per-kernel timings of one dQ mode."""
     # the first launches after another workload's run come at a lower clock
-    ms = time_loop(run, steps, torch, 8)
+    settle(run, torch, SETTLE_S)
+    ms = time_loop(run, steps, torch, 2)
     med = step_times(run, steps, torch)[steps // 2]
     k_dkdv = time_loop(lambda: run(["dkdv"]), steps, torch, 2)
     k_dq = time_loop(lambda: run(["preprocess", "dq"]), steps, torch, 2)
@@ -407,21 +475,26 @@ def main():
     def fwd_step():
         attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal, out=o, lse=lse)
 
+    # the clock settles under sustained load first (see settle()), then the
+    # W warmup steps
+    settle_steps, settle_s = settle(bwd_step, torch, SETTLE_S)
     for _ in range(args.warmup):
         fwd_step()
         bwd_step()
     torch.cuda.synchronize()
-    print("bench: warmup done", file=sys.stderr, flush=True)
+    print(f"bench: clock settled ({settle_steps} steps, {settle_s:.2f} s), warmup done",
+          file=sys.stderr, flush=True)
 
     # timed region: K backward steps, bracketed by device synchronisation
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ms = time_loop(bwd_step, args.steps, torch)
     t_wall = time.perf_counter() - t_wall
+    # the spread of single steps (L2 not flushed between steps), right after
+    # the timed loop: an idle gap (a host synchronisation) lowers the clock
+    per_step = step_times(bwd_step, args.steps, torch)
     print(f"bench: {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     ok = bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
-    # the spread of single steps (L2 not flushed between steps)
-    per_step = step_times(bwd_step, args.steps, torch)
 
     # per-kernel average launch durations (HIP events on the launch stream)
     kern_ms = {
@@ -486,6 +559,9 @@ def main():
         },
         "dkdv_tflops": round(dk_tf, 2),
         "hbm_algorithmic_GBps": round(bwd_bytes(w) / (ms * 1e-3) / 1e9, 1),
+        "settle": {"steps": settle_steps, "seconds": round(settle_s, 3),
+                   "note": "untimed backward steps run until the GPU clock settles, "
+                           "before the warmup steps"},
         "outputs_finite": ok,
         "wall_s_timed": round(t_wall, 3),
     }
