@@ -496,7 +496,9 @@ def main():
     print(f"bench: {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     ok = bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
 
-    # per-kernel average launch durations (HIP events on the launch stream)
+    # per-kernel average launch durations (HIP events on the launch stream),
+    # on a settled clock again after the host synchronisation above
+    settle(bwd_step, torch, SETTLE_S)
     kern_ms = {
         "preprocess": time_loop(lambda: bwd_step(["preprocess"]), args.steps, torch, 3),
         "dkdv": time_loop(lambda: bwd_step(["dkdv"]), args.steps, torch, 3),
