@@ -1,7 +1,8 @@
 // dK/dV kernel of backward attention on 16-bit MFMA (bf16 or f16 inputs,
-// float32 accumulation), shared by two objects: attn_bwd_mfma.hip builds it
-// without dQ work, attn_bwd_dkdv_dqa.hip with the fused dQ contribution
-// below.
+// float32 accumulation), shared by three objects: attn_bwd_mfma.hip builds
+// it without dQ work, attn_bwd_dkdv_dqa.hip with the fused dQ contribution
+// below (DQA), attn_bwd_dkdv_dss.hip writing its dS to the workspace for
+// the dQ-from-dS pass (DSS).
 //
 // One workgroup per 256 keys of a head (64 per wave) walks the query tiles,
 // recomputes S = Q K^T and P, and accumulates dV += P^T dO and dK += dS^T Q
