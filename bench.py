@@ -48,7 +48,7 @@ KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip"
                   "attn_launch.h", "attn_bwd_dkdv_dss.hip", "attn_bwd_dq_ds.hip")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "c978122f653f4dc21562c6d67e8115c631aa3420725bc194b661c724d15a0590",
+    "sources_sha256": "30c5c9f36a30ea47f75bee3dcb6a5d230528cdb06244a50ed1eaa15974d47c0e",
     "bytes": {"bwd_dkdv": 7.6447e+08},
 }
 
