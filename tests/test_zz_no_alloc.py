@@ -35,9 +35,14 @@ def test_rejects_problems_beyond_the_static_scratch():
     # 64 * 32 * 4096 rows of D and LSE2 (8 bytes each) = 64 MiB > 16 MiB
     args = [fake] * 9 + [None, None, 64, 32, 4096, 4096, 128, 128, 0.088, B.ATTN_MASK_CAUSAL,
                          B.ATTN_LAYOUT_BHSD, B.ATTN_BF16]
-    for mode in (B.ATTN_DQ_AUTO, B.ATTN_DQ_SEPARATE, B.ATTN_DQ_ATOMIC):
+    for mode in (B.ATTN_DQ_AUTO, B.ATTN_DQ_SEPARATE, B.ATTN_DQ_ATOMIC, B.ATTN_DQ_STORED_DS):
         st = lib.attn_bwd_ex_noalloc(*args, mode, None)
         assert st == B.ATTN_ESCRATCH, (mode, st)
+    # the stored-dS tiles of 2 x 32 heads at 4096 (1.1 GB) exceed it as well,
+    # while the automatic mode (the separate pass, 2 MiB of rows) fits
+    small_ds = [fake] * 9 + [None, None, 2, 32, 4096, 4096, 128, 128, 0.088,
+                             B.ATTN_MASK_CAUSAL, B.ATTN_LAYOUT_BHSD, B.ATTN_BF16]
+    assert lib.attn_bwd_ex_noalloc(*small_ds, B.ATTN_DQ_STORED_DS, None) == B.ATTN_ESCRATCH
     # the atomic mode's accumulator: 64 heads * 4096 rows * 128 floats = 128 MiB
     small = [fake] * 9 + [None, None, 2, 32, 4096, 4096, 128, 128, 0.088, B.ATTN_MASK_CAUSAL,
                           B.ATTN_LAYOUT_BHSD, B.ATTN_BF16]
