@@ -425,6 +425,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--dq-mode", default="auto", choices=("auto", "separate", "stored_ds"),
+                    help="dQ mode of the headline line (default: the library's own choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0)
     ap.add_argument("--no-proj", action="store_true", help="skip the projection-gradient timing")
@@ -461,16 +463,17 @@ def main():
     inputs_cpu = make_inputs(w, "cpu")
     q, k, v, do = (t.to(dev) for t in inputs_cpu)
     o, lse = attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal)
-    # the library's own choice of dQ mode (ATTN_DQ_AUTO) is what is timed
-    mode = resolved_mode(attn, w, q.dtype)
+    # the library's own choice of dQ mode (ATTN_DQ_AUTO) is what is timed,
+    # unless --dq-mode names another (for profiling the other modes)
+    mode = resolved_mode(attn, w, q.dtype) if args.dq_mode == "auto" else args.dq_mode
     ws = torch.empty(max(attn.bwd_workspace_bytes(w.B, w.H, w.n, w.m, w.d, w.dv, q.dtype,
-                                                  causal=w.causal), 1),
+                                                  dq_mode=args.dq_mode, causal=w.causal), 1),
                      dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
     def bwd_step(stages=None):
         attn.bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, workspace=ws,
-                 dq=dq, dk=dk, dv=dv, stages=stages)
+                 dq=dq, dk=dk, dv=dv, stages=stages, dq_mode=args.dq_mode)
 
     def fwd_step():
         attn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal, out=o, lse=lse)
@@ -556,7 +559,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name, f"bwd_{dominant}"),
+            # stored for the default mode's kernels only
+            "traffic": (measured_traffic(w.name, f"bwd_{dominant}") if mode == "separate"
+                        else None),
             "algorithmic_bytes": dom_bytes,
         },
         "dkdv_tflops": round(dk_tf, 2),
