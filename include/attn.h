@@ -192,9 +192,9 @@ size_t attn_bwd_workspace_bytes_ex(int B, int H, int n, int m, int d, int dv, in
                                    int dtype, int flags);
 
 /*
- * attn_bwd_workspace_bytes_ex without a mask argument: the size for
- * ATTN_MASK_NONE, which is at least the size for either causal mode, so it
- * suffices for attn_bwd and attn_bwd_ex with any mask.
+ * attn_bwd_workspace_bytes_ex without a mask argument: the largest size
+ * over the mask modes, so it suffices for attn_bwd and attn_bwd_ex with any
+ * mask.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags);

@@ -84,6 +84,14 @@ def test_workspace_size(lib):
                                                B.ATTN_MASK_CAUSAL_BOTTOM_RIGHT, code, sds) == \
             2 * 6 * 384 * 4 + 6 * 3 * tile
     assert lib.attn_bwd_workspace_bytes_ex(1, 1, 8, 8, 64, 64, 3, B.ATTN_BF16, 0) == 0  # bad mask
+    # the maskless size covers every mask: with more query than key blocks
+    # (1024 queries, 256 keys) the causal triangle indexes more tiles (10)
+    # than the dense layout (4)
+    for mask, tiles in ((B.ATTN_MASK_NONE, 4), (B.ATTN_MASK_CAUSAL, 10)):
+        assert lib.attn_bwd_workspace_bytes_ex(1, 1, 1024, 256, 64, 64, mask, B.ATTN_BF16,
+                                               sds) == 2 * 1024 * 4 + tiles * tile
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1024, 256, 64, 64, B.ATTN_BF16, sds) == \
+        2 * 1024 * 4 + 10 * tile
     # float32 has no fused dQ and no stored dS: nothing beyond the rows in
     # the automatic mode
     assert lib.attn_bwd_workspace_bytes(2, 3, 300, 300, 64, 64, B.ATTN_F32, 0) == 2 * 6 * 384 * 4

@@ -109,6 +109,10 @@ MASK_CASES = [
      [600, 300], 93, "bshd"),
     ("rows_without_keys_tl", 1, 2, 400, 300, 128, 128, "bf16", "causal_bottom_right", [400],
      [260], 94, "bhsd"),
+    # top-left causal with more query than key blocks: the stored-dS
+    # triangle indexes tiles past the dense layout's count
+    ("causal_tl_600x300", 1, 2, 600, 300, 128, 128, "bf16", "causal", [600], [300], 99,
+     "bhsd"),
 ]
 
 

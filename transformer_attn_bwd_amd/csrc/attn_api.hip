@@ -355,8 +355,13 @@ size_t attn_bwd_workspace_bytes_ex(int B, int H, int n, int m, int d, int dv, in
 
 size_t attn_bwd_workspace_bytes(int B, int H, int n, int m, int d, int dv, int dtype,
                                 int flags) {
-    // without the mask: the larger (unmasked, dense) stored-dS layout
-    return attn_bwd_workspace_bytes_ex(B, H, n, m, d, dv, ATTN_MASK_NONE, dtype, flags);
+    // without the mask: enough for every mask mode (the dense stored-dS
+    // layout is the larger one unless there are more query than key blocks)
+    const size_t dense =
+        attn_bwd_workspace_bytes_ex(B, H, n, m, d, dv, ATTN_MASK_NONE, dtype, flags);
+    const size_t tri =
+        attn_bwd_workspace_bytes_ex(B, H, n, m, d, dv, ATTN_MASK_CAUSAL, dtype, flags);
+    return dense > tri ? dense : tri;
 }
 
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
