@@ -37,7 +37,12 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3     # MI355X float32 vector peak (the float32 path runs on VALU)
 SETTLE_S = 0.25             # seconds of back-to-back backward steps before any timing
+
+
+def peak_tflops(w) -> float:
+    return PEAK_F32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
 
 # HBM bytes per launch of the dK/dV kernel (the dominant one) on causal_4k_d128, from
 # rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the
@@ -315,7 +320,7 @@ def proj_bench(w, steps, torch, attn):
 
 
 # the other workloads timed beside the headline, in both dQ modes
-TABLE_WORKLOADS = ("causal_1k_d64", "causal_4k_d128", "causal_16k_d128",
+TABLE_WORKLOADS = ("head_64_fp32", "causal_1k_d64", "causal_4k_d128", "causal_16k_d128",
                    "cross_512x2048_d128_dv64", "causal_4k_d128_fp16")
 
 
@@ -340,14 +345,14 @@ def mode_figures(w, run, steps, torch, split=None, mode="separate"):
     kern = {"dkdv": (k_dkdv, f_dkdv), "dq": (k_dq, f_dq)}
     dom = max(kern, key=lambda k_: kern[k_][0])
     tf = bwd_flops(w) / (ms * 1e-3) / 1e12
+    peak = peak_tflops(w)
     out = {
         "ms_mean": round(ms, 4), "ms_median": round(med, 4), "tflops": round(tf, 2),
-        "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * tf / peak, 2), "peak_tflops": peak,
         "kernels_ms": {"dkdv": round(k_dkdv, 4), "dq_with_preprocess": round(k_dq, 4)},
         "dominant": dom,
         "dominant_share_of_step": round(kern[dom][0] / ms, 3),
-        "dominant_frac_of_peak": round(kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
-                                       / PEAK_BF16_TFLOPS, 4),
+        "dominant_frac_of_peak": round(kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12 / peak, 4),
     }
     if split is not None:
         out["split"] = split
@@ -357,7 +362,9 @@ def mode_figures(w, run, steps, torch, split=None, mode="separate"):
 def workload_table(names, steps, torch, attn, make_inputs, workloads):
     """For each workload: the backward in the separate-pass and stored-dS dQ
     modes, and in the atomic mode at the best of a few splits (leading
-    256-key blocks left to the separate pass)."""
+    256-key blocks left to the separate pass); the float32 workload in the
+    separate pass only (the other modes are 16-bit), against the float32
+    vector peak."""
     table = {}
     dev = "cuda:0"
     for name in names:
@@ -379,9 +386,12 @@ def workload_table(names, steps, torch, attn, make_inputs, workloads):
                 dq_split=split, workspace=wss[key], dq=dq, dk=dk, dv=dv, stages=stages)
 
         row = {"flops": bwd_flops(w), "auto_mode": resolved_mode(attn, w, q.dtype),
-               "separate": mode_figures(w, runner("separate", None), steps, torch),
-               "stored_ds": mode_figures(w, runner("stored_ds", None), steps, torch,
-                                         mode="stored_ds")}
+               "separate": mode_figures(w, runner("separate", None), steps, torch)}
+        if w.dtype == "fp32":
+            table[name] = row
+            continue
+        row["stored_ds"] = mode_figures(w, runner("stored_ds", None), steps, torch,
+                                        mode="stored_ds")
         nkb = (w.m + 255) // 256
         splits = sorted({0} | {max(1, (nkb * f) // 8) for f in (1, 2, 3, 4, 6)})
         tried = {sp: time_loop(runner("atomic", sp), max(3, steps // 2), torch, 2)
@@ -527,7 +537,8 @@ def main():
     dims = f"d={w.d}" if w.d == w.dv else f"d={w.d}, dv={w.dv}"
 
     result = {
-        "metric": f"attn backward TFLOP/s ({w.dtype}, {mask}, {dims}, {shape}) + % of MFMA peak",
+        "metric": f"attn backward TFLOP/s ({w.dtype}, {mask}, {dims}, {shape}) + % of "
+                  + ("float32 vector peak" if w.dtype == "fp32" else "MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -544,21 +555,22 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "m": w.m, "d": w.d,
                    "dv": w.dv, "causal": w.causal, "seed": w.seed, "scale": w.softmax_scale,
                    "parallelism": "single GPU"},
-        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * tflops / peak_tflops(w), 2),
         "flops_per_step": flops,
         "dq_mode": mode,
         "kernels_ms": {k_: round(v_, 4) for k_, v_ in kern_ms.items()},
         "fwd": {"ms": round(fwd_ms, 4),
                 "tflops": round(fwd_flops(w) / (fwd_ms * 1e-3) / 1e12, 2),
                 "pct_of_peak": round(100.0 * fwd_flops(w) / (fwd_ms * 1e-3) / 1e12
-                                     / PEAK_BF16_TFLOPS, 2)},
+                                     / peak_tflops(w), 2)},
         "roofline": {
             "kernel": f"bwd_{dominant}",
-            "bound": roofline_bound(dom_flops, dom_bytes),
+            # the float32 path runs on the vector ALUs, not the matrix cores
+            "bound": "alu" if w.dtype == "fp32" else roofline_bound(dom_flops, dom_bytes),
             "achieved": round(dom_tf, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak_tflops(w),
             "unit": "TFLOP/s",
-            "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dom_tf / peak_tflops(w), 4),
             # stored for the default mode's kernels only
             "traffic": (measured_traffic(w.name, f"bwd_{dominant}") if mode == "separate"
                         else None),
