@@ -53,7 +53,7 @@ KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip"
                   "attn_launch.h", "attn_bwd_dkdv_dss.hip", "attn_bwd_dq_ds.hip")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "30c5c9f36a30ea47f75bee3dcb6a5d230528cdb06244a50ed1eaa15974d47c0e",
+    "sources_sha256": "800c5d2e9dd0efe16d1e10b9613d42c5c05947dc7899e8c26220352acd301315",
     "bytes": {"bwd_dkdv": 7.6447e+08},
 }
 

@@ -13,7 +13,8 @@
 // Layout: four waves, wave w owning queries i0 + 64w .. +63 (two 32-query
 // MFMA tiles).  Per 64-key step the K rows go to LDS for every wave and
 // each wave's 64 x 64 block of dS^T to its own part of LDS, both by buffer
-// loads straight into swizzled tiles, three steps in flight.  Both operands
+// loads straight into swizzled tiles, three LDS stages with the fills two
+// steps ahead.  Both operands
 // come out of LDS with transposing reads: K^T (rows = d, k = keys) and
 // dS^T (k = keys, columns = queries) in the same row-of-C key order
 // (attn_device.h), so their product is dQ^T.  Causal masking needs no work
