@@ -53,7 +53,7 @@ KERNEL_SOURCES = ("attn_bwd_mfma.hip", "attn_bwd_dkdv.h", "attn_bwd_dq_mfma.hip"
                   "attn_launch.h", "attn_bwd_dkdv_dss.hip", "attn_bwd_dq_ds.hip")
 MEASURED_TRAFFIC = {
     "workload": "causal_4k_d128",
-    "sources_sha256": "800c5d2e9dd0efe16d1e10b9613d42c5c05947dc7899e8c26220352acd301315",
+    "sources_sha256": "ecdfe459ee4e70701903f2e95d83000f83945d4f61cdae6ed5e74e1b09fca7af",
     "bytes": {"bwd_dkdv": 7.6447e+08},
 }
 

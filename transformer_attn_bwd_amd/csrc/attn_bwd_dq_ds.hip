@@ -14,11 +14,11 @@
 // MFMA tiles).  Per 64-key step the K rows go to LDS for every wave and
 // each wave's 64 x 64 block of dS^T to its own part of LDS, both by buffer
 // loads straight into swizzled tiles, three LDS stages with the fills two
-// steps ahead.  Both operands
-// come out of LDS with transposing reads: K^T (rows = d, k = keys) and
-// dS^T (k = keys, columns = queries) in the same row-of-C key order
-// (attn_device.h), so their product is dQ^T.  Causal masking needs no work
-// here: the stored dS is exactly zero above the diagonal.
+// steps ahead.  Both operands come out of LDS with transposing reads: K^T
+// (rows = d, k = keys) and dS^T (k = keys, columns = queries) in the same
+// row-of-C key order (attn_device.h), so their product is dQ^T.  Causal
+// masking needs no work here: the stored dS is exactly zero above the
+// diagonal.
 #include "attn_device.h"
 #include "attn_launch.h"
 
