@@ -241,8 +241,20 @@ class _FenceFreeEvents:
 
 def step_times(fn, steps, torch):
     """Per-step durations (ms) from a fence-free event pair around each of
-    `steps` back-to-back steps, sorted."""
-    ev = _FenceFreeEvents(torch)
+    `steps` back-to-back steps, sorted (torch's events if the HIP runtime's
+    symbols cannot be reached)."""
+    try:
+        ev = _FenceFreeEvents(torch)
+    except OSError:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
     torch.cuda.synchronize()
     for a, b in pairs:
