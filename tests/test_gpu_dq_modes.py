@@ -113,6 +113,9 @@ MASK_CASES = [
     # triangle indexes tiles past the dense layout's count
     ("causal_tl_600x300", 1, 2, 600, 300, 128, 128, "bf16", "causal", [600], [300], 99,
      "bhsd"),
+    # causal with per-batch lengths in the [B, seq, H, dim] layout, fp16, d != dv
+    ("varlen_causal_bshd_f16_d64_dv128", 2, 2, 520, 520, 64, 128, "fp16", "causal",
+     [520, 300], [520, 300], 100, "bshd"),
 ]
 
 
